@@ -1,0 +1,181 @@
+"""ctypes wrapper over the fp64 CPU oracle (oracle/orc.c).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import this
+package.  It shares no code with the HIP library ``block_sparse_local_amd``
+and never imports it.
+
+Every function takes numpy arrays on the host.  Q, K, V are float32 arrays of
+shape [batch, heads, n, d] holding the exact (bf16- or fp32-rounded) values a
+GPU consumes; results are float64.  The computation follows the NucleoByte
+project page, section 3 ("Localized Block-Sparse Attention Matrix" for the
+band rule, "Softmax Normalization & Online Numerical Stability" for the scores
+and the softmax); see orc.c for the definitions.
+
+Parity pins (what ties each routine to something other than itself) live in
+``tests/test_oracle_*.py``.  No oracle routine is "parity unpinned".
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _declare(lib):
+    i = ctypes.c_int
+    lib.orc_version.restype = i
+    lib.orc_active_blocks.argtypes = [i, i, i, i, i, _i32p, _i32p]
+    lib.orc_masks.argtypes = [i, i, i, i, i, _i32p, _i32p, _u32p]
+    lib.orc_forward_f64.argtypes = [i, i, i, i, i, i, i, ctypes.c_double, _i32p, _f32p, _f32p,
+                                    _f32p, _f64p, _f64p, _f64p, i]
+    lib.orc_forward_blocks_f64.argtypes = [i, i, i, i, i, i, i, ctypes.c_double, _i32p, _f32p,
+                                           _f32p, _f32p, ctypes.c_int64, _i32p, _f64p, _f64p,
+                                           _f64p, i]
+    lib.orc_forward_recurrence_f64.argtypes = [i, i, i, i, i, i, i, ctypes.c_double, _i32p,
+                                               _f32p, _f32p, _f32p, _f64p]
+    for name in ("orc_active_blocks", "orc_masks", "orc_forward_f64", "orc_forward_blocks_f64",
+                 "orc_forward_recurrence_f64"):
+        getattr(lib, name).restype = i
+    return lib
+
+
+def load(path=None):
+    """Load liborc.so (compiling it with gcc if it is missing); ``path`` loads
+    another build, e.g. a mutant compiled by the mutation tests."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    if _lib is None:
+        lib_path = os.path.join(_HERE, "liborc.so")
+        if not os.path.exists(lib_path):
+            _build.build()
+        _lib = _declare(ctypes.CDLL(lib_path))
+    return _lib
+
+
+def default_threads():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _ptr(a, typ):
+    return None if a is None else a.ctypes.data_as(typ)
+
+
+def _lens(batch, n, seqlens):
+    if seqlens is None:
+        return None
+    s = np.ascontiguousarray(seqlens, dtype=np.int32)
+    if s.shape != (batch,):
+        raise ValueError("seqlens must have shape [batch]")
+    return s
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise OracleError(f"{name} failed with code {rc}")
+
+
+def active_blocks(batch, n, bsize, radius, causal, seqlens=None, lib=None):
+    """int32 [batch, n/bsize, 2R+1]: ascending visited key blocks, -1 padded."""
+    lib = lib or load()
+    s = _lens(batch, n, seqlens)
+    nblk = n // bsize if bsize > 0 else 0
+    out = np.full((batch, nblk, max(2 * radius + 1, 1)), -7, dtype=np.int32)
+    _check(lib.orc_active_blocks(batch, n, bsize, radius, int(causal), _ptr(s, _i32p),
+                                 _ptr(out, _i32p)), "orc_active_blocks")
+    return out
+
+
+def masks(batch, n, bsize, radius, causal, seqlens=None, active=None, lib=None):
+    """uint32 [batch, n/bsize, 2R+1, bsize]: word r bit c set iff key c of the
+    slot's key block is kept for query row r of the query block."""
+    lib = lib or load()
+    s = _lens(batch, n, seqlens)
+    if active is None:
+        active = active_blocks(batch, n, bsize, radius, causal, seqlens, lib=lib)
+    active = np.ascontiguousarray(active, dtype=np.int32)
+    out = np.zeros(active.shape + (bsize,), dtype=np.uint32)
+    _check(lib.orc_masks(batch, n, bsize, radius, int(causal), _ptr(s, _i32p),
+                         _ptr(active, _i32p), _ptr(out, _u32p)), "orc_masks")
+    return out
+
+
+def _f32(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.float32:
+        raise TypeError("oracle inputs are float32 arrays holding the exact input values")
+    return a
+
+
+def forward(q, k, v, seqlens=None, bsize=32, radius=1, causal=False, scale=0.0, nthreads=None,
+            lib=None):
+    """Two-pass definition.  Returns (o [b,h,n,d], lse [b,h,n], psum [b,h,n])
+    in float64; psum is the sum of each row's normalised probabilities."""
+    lib = lib or load()
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    batch, heads, n, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v shapes differ")
+    s = _lens(batch, n, seqlens)
+    o = np.empty((batch, heads, n, d), dtype=np.float64)
+    lse = np.empty((batch, heads, n), dtype=np.float64)
+    psum = np.empty((batch, heads, n), dtype=np.float64)
+    _check(lib.orc_forward_f64(batch, heads, n, d, bsize, radius, int(causal), float(scale),
+                               _ptr(s, _i32p), _ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p),
+                               _ptr(o, _f64p), _ptr(lse, _f64p), _ptr(psum, _f64p),
+                               nthreads or default_threads()), "orc_forward_f64")
+    return o, lse, psum
+
+
+def forward_blocks(q, k, v, sel, seqlens=None, bsize=32, radius=1, causal=False, scale=0.0,
+                   nthreads=None, lib=None):
+    """Only the query blocks listed in ``sel`` (int array [m, 3] of (b, h, i)).
+    Returns (o [m, bsize, d], lse [m, bsize], psum [m, bsize])."""
+    lib = lib or load()
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    batch, heads, n, d = q.shape
+    s = _lens(batch, n, seqlens)
+    sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 3)
+    m = sel.shape[0]
+    o = np.empty((m, bsize, d), dtype=np.float64)
+    lse = np.empty((m, bsize), dtype=np.float64)
+    psum = np.empty((m, bsize), dtype=np.float64)
+    _check(lib.orc_forward_blocks_f64(batch, heads, n, d, bsize, radius, int(causal),
+                                      float(scale), _ptr(s, _i32p), _ptr(q, _f32p),
+                                      _ptr(k, _f32p), _ptr(v, _f32p), m, _ptr(sel, _i32p),
+                                      _ptr(o, _f64p), _ptr(lse, _f64p), _ptr(psum, _f64p),
+                                      nthreads or default_threads()), "orc_forward_blocks_f64")
+    return o, lse, psum
+
+
+def forward_recurrence(q, k, v, seqlens=None, bsize=32, radius=1, causal=False, scale=0.0,
+                       lib=None):
+    """The page's running (m, d, O) recurrence, block by block, divided by d at
+    the end.  Single threaded; meant for small inputs."""
+    lib = lib or load()
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    batch, heads, n, d = q.shape
+    s = _lens(batch, n, seqlens)
+    o = np.empty((batch, heads, n, d), dtype=np.float64)
+    _check(lib.orc_forward_recurrence_f64(batch, heads, n, d, bsize, radius, int(causal),
+                                          float(scale), _ptr(s, _i32p), _ptr(q, _f32p),
+                                          _ptr(k, _f32p), _ptr(v, _f32p), _ptr(o, _f64p)),
+           "orc_forward_recurrence_f64")
+    return o

@@ -1,0 +1,495 @@
+/*
+ * orc.c -- plain fp64 CPU oracle for the banded block-sparse attention forward.
+ *
+ * TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or helper with the HIP library, and it never touches a GPU.
+ *
+ * What it computes follows the NucleoByte project page ("NucleoByte:
+ * GPU-Accelerated Block-Sparse Genomic Language Model"):
+ *   - section 3, "Localized Block-Sparse Attention Matrix": with block size B,
+ *     query block i scores only key blocks j with |i - j| <= R;
+ *   - section 3, "Softmax Normalization & Online Numerical Stability": scores
+ *     S = Q K^T / sqrt(d_k) followed by a softmax over the scored keys, kept
+ *     stable by a running maximum, a running denominator and a running output;
+ *   - section 2, item 2 ("Dynamic Ceiling Hardware Alignment"): each batch is
+ *     padded up to a multiple of the block size, so keys past a sequence's
+ *     length are padding and are never attended to.
+ *
+ * The online recurrence on that page is an exact rewriting of an ordinary
+ * softmax, so the main routine here is the plain definition, done in two passes
+ * per query row over the set of keys the row may attend to:
+ *
+ *   A(b,t) = { s : 0 <= s < len_b,  |floor(t/B) - floor(s/B)| <= R,
+ *              and s <= t when the causal flag is set }
+ *   S_ts   = scale * sum_c Q[b,h,t,c] K[b,h,s,c]
+ *   O[b,h,t,:] = sum_{s in A} exp(S_ts - M_t) V[b,h,s,:] / sum_{s in A} exp(S_ts - M_t)
+ *   M_t    = max_{s in A} S_ts,   lse_t = M_t + ln sum_{s in A} exp(S_ts - M_t)
+ *   rows t >= len_b are padding: O = 0, lse = -inf.
+ *
+ * A second routine, orc_forward_recurrence_f64, walks the page's running
+ * (m, d, O) update block by block, in the page's order, and divides by the
+ * denominator once after the last block (the page never writes that division;
+ * it is the only reading under which the probabilities sum to one).  The tests
+ * compare the two routines; they are independent formulations of one result.
+ *
+ * Inputs are float (the exact bf16- or fp32-rounded values a GPU consumes);
+ * every product and sum is taken in double.  Q, K, V, O are [batch][heads][n][d]
+ * contiguous.  All routines return 0 on success and a negative code on bad
+ * arguments, before writing anything.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_E_INVALID (-1)
+#define ORC_E_NOMEM (-2)
+
+int orc_version(void) { return 1; }
+
+/* ---------------------------------------------------------------- validation */
+
+static int check_shape(int batch, int n, int bsize, int radius, const int32_t *seqlens)
+{
+    if (batch < 0 || n < 0 || bsize < 1 || radius < 0)
+        return ORC_E_INVALID;
+    if (n % bsize != 0)
+        return ORC_E_INVALID;
+    if (seqlens) {
+        for (int b = 0; b < batch; ++b)
+            if (seqlens[b] < 0 || seqlens[b] > n)
+                return ORC_E_INVALID;
+    }
+    return 0;
+}
+
+static int seq_len(const int32_t *seqlens, int b, int n) { return seqlens ? seqlens[b] : n; }
+
+/* Number of blocks that hold at least one real token: the padded length of a
+ * sequence rounded up to the block size, divided by it (section 2, item 2). */
+static int blocks_of(int len, int bsize) { return (len + bsize - 1) / bsize; }
+
+/* Is key block j in the band of query block i, inside the sequence, and (causal)
+ * not after i?  Section 3's band rule |i - j| <= R. */
+static int block_in_band(int i, int j, int radius, int nb, int causal)
+{
+    if (i >= nb || j < 0 || j >= nb)
+        return 0;
+    if (abs(i - j) > radius)
+        return 0;
+    if (causal && j > i)
+        return 0;
+    return 1;
+}
+
+/* Is token pair (query t, key s) kept: the token-level set A(b,t) above. */
+static int pair_kept(int t, int s, int len, int bsize, int radius, int causal)
+{
+    if (t < 0 || t >= len || s < 0 || s >= len)
+        return 0;
+    if (abs(t / bsize - s / bsize) > radius)
+        return 0;
+    if (causal && s > t)
+        return 0;
+    return 1;
+}
+
+/* ------------------------------------------------------------- block lists */
+
+/* active[b][i][0 .. 2R]: the key blocks query block i of sequence b visits, in
+ * ascending order, padded with -1.  Empty (all -1) for blocks that hold no real
+ * token. */
+int orc_active_blocks(int batch, int n, int bsize, int radius, int causal,
+                      const int32_t *seqlens, int32_t *active)
+{
+    int rc = check_shape(batch, n, bsize, radius, seqlens);
+    if (rc)
+        return rc;
+    if (batch > 0 && n > 0 && !active)
+        return ORC_E_INVALID;
+    const int nblk = n / bsize, width = 2 * radius + 1;
+    for (int b = 0; b < batch; ++b) {
+        const int nb = blocks_of(seq_len(seqlens, b, n), bsize);
+        for (int i = 0; i < nblk; ++i) {
+            int32_t *row = active + ((int64_t)b * nblk + i) * width;
+            int used = 0;
+            for (int j = i - radius; j <= i + radius; ++j)
+                if (block_in_band(i, j, radius, nb, causal))
+                    row[used++] = j;
+            for (; used < width; ++used)
+                row[used] = -1;
+        }
+    }
+    return 0;
+}
+
+/* masks[b][i][slot][r], bit c: for the slot-th active key block j of query block
+ * i, key j*B + c is kept for query i*B + r.  Zero for unused slots and for query
+ * rows past the sequence.  Needs B <= 32 (one 32-bit word per query row). */
+int orc_masks(int batch, int n, int bsize, int radius, int causal, const int32_t *seqlens,
+              const int32_t *active, uint32_t *masks)
+{
+    int rc = check_shape(batch, n, bsize, radius, seqlens);
+    if (rc)
+        return rc;
+    if (bsize > 32)
+        return ORC_E_INVALID;
+    if (batch > 0 && n > 0 && (!active || !masks))
+        return ORC_E_INVALID;
+    const int nblk = n / bsize, width = 2 * radius + 1;
+    for (int b = 0; b < batch; ++b) {
+        const int len = seq_len(seqlens, b, n);
+        for (int i = 0; i < nblk; ++i) {
+            for (int slot = 0; slot < width; ++slot) {
+                const int64_t at = ((int64_t)b * nblk + i) * width + slot;
+                const int j = active[at];
+                uint32_t *words = masks + at * bsize;
+                for (int r = 0; r < bsize; ++r) {
+                    uint32_t w = 0;
+                    if (j >= 0)
+                        for (int c = 0; c < bsize; ++c)
+                            if (pair_kept(i * bsize + r, j * bsize + c, len, bsize, radius, causal))
+                                w |= (uint32_t)1 << c;
+                    words[r] = w;
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* --------------------------------------------------- two-pass definition */
+
+typedef struct {
+    int batch, heads, n, d, bsize, radius, causal;
+    double scale;
+    const int32_t *seqlens;
+    const float *q, *k, *v;
+} problem;
+
+/* One query row t of (b, h): the plain definition above.  o_row gets d values;
+ * *lse and *psum (sum of the normalised probabilities) may be NULL. */
+static void row_definition(const problem *p, int b, int h, int t, double *sbuf,
+                           int32_t *sidx, double *o_row, double *lse, double *psum)
+{
+    const int len = seq_len(p->seqlens, b, p->n);
+    const int64_t base = ((int64_t)b * p->heads + h) * p->n;
+    const int d = p->d;
+    if (t >= len) {
+        for (int c = 0; c < d; ++c)
+            o_row[c] = 0.0;
+        if (lse)
+            *lse = -INFINITY;
+        if (psum)
+            *psum = 0.0;
+        return;
+    }
+    /* keys that can be in A(b,t): the blocks within R of t's block */
+    const int ib = t / p->bsize;
+    int s_lo = (ib - p->radius) * p->bsize;
+    int s_hi = (ib + p->radius + 1) * p->bsize; /* exclusive */
+    if (s_lo < 0)
+        s_lo = 0;
+    if (s_hi > len)
+        s_hi = len;
+    const float *qt = p->q + (base + t) * d;
+
+    /* pass 1: scores of every kept key, and their maximum */
+    int cnt = 0;
+    double m = -INFINITY;
+    for (int s = s_lo; s < s_hi; ++s) {
+        if (!pair_kept(t, s, len, p->bsize, p->radius, p->causal))
+            continue;
+        const float *ks = p->k + (base + s) * d;
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c)
+            dot += (double)qt[c] * (double)ks[c];
+        const double sc = p->scale * dot;
+        sbuf[cnt] = sc;
+        sidx[cnt] = s;
+        ++cnt;
+        if (sc > m)
+            m = sc;
+    }
+    /* pass 2: exponentials, denominator, weighted sum of values */
+    double l = 0.0;
+    for (int c = 0; c < d; ++c)
+        o_row[c] = 0.0;
+    for (int e = 0; e < cnt; ++e) {
+        const double w = exp(sbuf[e] - m);
+        sbuf[e] = w;
+        l += w;
+        const float *vs = p->v + (base + sidx[e]) * d;
+        for (int c = 0; c < d; ++c)
+            o_row[c] += w * (double)vs[c];
+    }
+    for (int c = 0; c < d; ++c)
+        o_row[c] /= l;
+    if (lse)
+        *lse = m + log(l);
+    if (psum) {
+        double ps = 0.0;
+        for (int e = 0; e < cnt; ++e)
+            ps += sbuf[e] / l;
+        *psum = ps;
+    }
+}
+
+/* Work list for the thread pool: query blocks given as (b, h, i) triples.  Each
+ * output row block is [bsize][d] (o), [bsize] (lse, psum). */
+typedef struct {
+    const problem *p;
+    int64_t nsel;
+    const int32_t *sel; /* [nsel][3] or NULL = every block in order */
+    double *o, *lse, *psum;
+    int64_t next;
+    pthread_mutex_t lock;
+    int failed;
+} job;
+
+static int64_t take(job *jb, int64_t chunk, int64_t *end)
+{
+    pthread_mutex_lock(&jb->lock);
+    int64_t at = jb->next;
+    jb->next += chunk;
+    pthread_mutex_unlock(&jb->lock);
+    *end = at + chunk < jb->nsel ? at + chunk : jb->nsel;
+    return at;
+}
+
+static void *worker(void *arg)
+{
+    job *jb = (job *)arg;
+    const problem *p = jb->p;
+    const int nblk = p->n / p->bsize;
+    const int maxkeys = (2 * p->radius + 1) * p->bsize;
+    double *sbuf = (double *)malloc(sizeof(double) * (size_t)maxkeys);
+    int32_t *sidx = (int32_t *)malloc(sizeof(int32_t) * (size_t)maxkeys);
+    if (!sbuf || !sidx) {
+        free(sbuf);
+        free(sidx);
+        pthread_mutex_lock(&jb->lock);
+        jb->failed = 1;
+        pthread_mutex_unlock(&jb->lock);
+        return NULL;
+    }
+    for (;;) {
+        int64_t end, at = take(jb, 4, &end);
+        if (at >= jb->nsel)
+            break;
+        for (int64_t w = at; w < end; ++w) {
+            int b, h, i;
+            if (jb->sel) {
+                b = jb->sel[3 * w];
+                h = jb->sel[3 * w + 1];
+                i = jb->sel[3 * w + 2];
+            } else {
+                i = (int)(w % nblk);
+                h = (int)((w / nblk) % p->heads);
+                b = (int)(w / ((int64_t)nblk * p->heads));
+            }
+            for (int r = 0; r < p->bsize; ++r) {
+                const int64_t row = w * p->bsize + r;
+                row_definition(p, b, h, i * p->bsize + r, sbuf, sidx, jb->o + row * p->d,
+                               jb->lse ? jb->lse + row : NULL, jb->psum ? jb->psum + row : NULL);
+            }
+        }
+    }
+    free(sbuf);
+    free(sidx);
+    return NULL;
+}
+
+static int run_pool(job *jb, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 1024)
+        nthreads = 1024;
+    pthread_mutex_init(&jb->lock, NULL);
+    jb->next = 0;
+    jb->failed = 0;
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!tid)
+        return ORC_E_NOMEM;
+    int started = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        if (pthread_create(&tid[t], NULL, worker, jb) != 0)
+            break;
+        ++started;
+    }
+    if (started == 0)
+        worker(jb);
+    for (int t = 0; t < started; ++t)
+        pthread_join(tid[t], NULL);
+    free(tid);
+    pthread_mutex_destroy(&jb->lock);
+    return jb->failed ? ORC_E_NOMEM : 0;
+}
+
+static int check_problem(const problem *p)
+{
+    int rc = check_shape(p->batch, p->n, p->bsize, p->radius, p->seqlens);
+    if (rc)
+        return rc;
+    if (p->heads < 0 || p->d < 1)
+        return ORC_E_INVALID;
+    if (!(p->scale > 0.0) || !isfinite(p->scale))
+        return ORC_E_INVALID;
+    return 0;
+}
+
+/* scale <= 0 selects 1/sqrt(d), the scaling of section 3's score formula. */
+static double pick_scale(double scale, int d) { return scale > 0.0 ? scale : 1.0 / sqrt((double)d); }
+
+/* Full forward: o [batch][heads][n][d], lse and psum [batch][heads][n] (either
+ * may be NULL). */
+int orc_forward_f64(int batch, int heads, int n, int d, int bsize, int radius, int causal,
+                    double scale, const int32_t *seqlens, const float *q, const float *k,
+                    const float *v, double *o, double *lse, double *psum, int nthreads)
+{
+    problem p = {batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v};
+    int rc = check_problem(&p);
+    if (rc)
+        return rc;
+    const int64_t nwork = (int64_t)batch * heads * (n / bsize);
+    if (nwork == 0)
+        return 0;
+    if (!q || !k || !v || !o)
+        return ORC_E_INVALID;
+    job jb;
+    memset(&jb, 0, sizeof jb);
+    jb.p = &p;
+    jb.nsel = nwork;
+    jb.sel = NULL;
+    jb.o = o;
+    jb.lse = lse;
+    jb.psum = psum;
+    return run_pool(&jb, nthreads);
+}
+
+/* Selected query blocks only: sel[w] = (b, h, i).  o [nsel][bsize][d], lse and
+ * psum [nsel][bsize].  The inputs are the full-size tensors. */
+int orc_forward_blocks_f64(int batch, int heads, int n, int d, int bsize, int radius, int causal,
+                           double scale, const int32_t *seqlens, const float *q, const float *k,
+                           const float *v, int64_t nsel, const int32_t *sel, double *o,
+                           double *lse, double *psum, int nthreads)
+{
+    problem p = {batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v};
+    int rc = check_problem(&p);
+    if (rc)
+        return rc;
+    if (nsel < 0)
+        return ORC_E_INVALID;
+    if (nsel == 0)
+        return 0;
+    if (!q || !k || !v || !o || !sel)
+        return ORC_E_INVALID;
+    for (int64_t w = 0; w < nsel; ++w) {
+        const int32_t *s = sel + 3 * w;
+        if (s[0] < 0 || s[0] >= batch || s[1] < 0 || s[1] >= heads || s[2] < 0 ||
+            s[2] >= n / bsize)
+            return ORC_E_INVALID;
+    }
+    job jb;
+    memset(&jb, 0, sizeof jb);
+    jb.p = &p;
+    jb.nsel = nsel;
+    jb.sel = sel;
+    jb.o = o;
+    jb.lse = lse;
+    jb.psum = psum;
+    return run_pool(&jb, nthreads);
+}
+
+/* ------------------------------------------- the page's running recurrence */
+
+/* Section 3's update taken block by block, in order of ascending key block:
+ *   m_new = max(m_old, max_c S_ic)
+ *   d_new = d_old * exp(m_old - m_new) + sum_c exp(S_ic - m_new)
+ *   O_new = O_old * exp(m_old - m_new) + sum_c exp(S_ic - m_new) V_c
+ * per query row, starting from m = -inf, d = 0, O = 0, with masked scores set to
+ * -inf; after the last block O / d is the output.  Single threaded. */
+int orc_forward_recurrence_f64(int batch, int heads, int n, int d, int bsize, int radius,
+                               int causal, double scale, const int32_t *seqlens, const float *q,
+                               const float *k, const float *v, double *o)
+{
+    problem p = {batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v};
+    int rc = check_problem(&p);
+    if (rc)
+        return rc;
+    const int nblk = n / bsize;
+    if ((int64_t)batch * heads * nblk == 0)
+        return 0;
+    if (!q || !k || !v || !o)
+        return ORC_E_INVALID;
+    double *sblk = (double *)malloc(sizeof(double) * (size_t)bsize);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+    if (!sblk || !acc) {
+        free(sblk);
+        free(acc);
+        return ORC_E_NOMEM;
+    }
+    for (int b = 0; b < batch; ++b) {
+        const int len = seq_len(seqlens, b, n);
+        const int nb = blocks_of(len, bsize);
+        for (int h = 0; h < heads; ++h) {
+            const int64_t base = ((int64_t)b * heads + h) * n;
+            for (int t = 0; t < n; ++t) {
+                double *out = o + (base + t) * d;
+                if (t >= len) {
+                    for (int c = 0; c < d; ++c)
+                        out[c] = 0.0;
+                    continue;
+                }
+                const int i = t / bsize;
+                double m_old = -INFINITY, den = 0.0;
+                for (int c = 0; c < d; ++c)
+                    acc[c] = 0.0;
+                for (int j = i - radius; j <= i + radius; ++j) {
+                    if (!block_in_band(i, j, radius, nb, causal))
+                        continue;
+                    double bmax = -INFINITY;
+                    for (int c = 0; c < bsize; ++c) {
+                        const int s = j * bsize + c;
+                        double sc = -INFINITY;
+                        if (pair_kept(t, s, len, bsize, radius, causal)) {
+                            double dot = 0.0;
+                            for (int e = 0; e < d; ++e)
+                                dot += (double)q[(base + t) * d + e] * (double)k[(base + s) * d + e];
+                            sc = p.scale * dot;
+                        }
+                        sblk[c] = sc;
+                        if (sc > bmax)
+                            bmax = sc;
+                    }
+                    const double m_new = bmax > m_old ? bmax : m_old;
+                    if (m_new == -INFINITY)
+                        continue; /* every key of this block masked: nothing to add */
+                    const double corr = exp(m_old - m_new); /* 0 on the first block */
+                    double add = 0.0;
+                    for (int e = 0; e < d; ++e)
+                        acc[e] *= corr;
+                    for (int c = 0; c < bsize; ++c) {
+                        const double w = exp(sblk[c] - m_new);
+                        if (w == 0.0)
+                            continue;
+                        add += w;
+                        const float *vs = v + (base + (int64_t)j * bsize + c) * d;
+                        for (int e = 0; e < d; ++e)
+                            acc[e] += w * (double)vs[e];
+                    }
+                    den = den * corr + add;
+                    m_old = m_new;
+                }
+                for (int c = 0; c < d; ++c)
+                    out[c] = acc[c] / den;
+            }
+        }
+    }
+    free(sblk);
+    free(acc);
+    return 0;
+}

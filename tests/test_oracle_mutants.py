@@ -1,0 +1,107 @@
+"""Are the oracle's pins strong enough?  (CPU only.)
+
+Each case below copies oracle/orc.c into a temporary directory, plants one
+plausible mistake (a dropped term, a wrong sign or bound, a swapped operand),
+compiles it and runs a small battery of the same pins the other oracle tests
+use.  Every mutant must fail at least one pin; the unmodified source must pass
+them all.
+"""
+import os
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import build as obuild
+from tests._brute import dense_reference, token_mask
+
+MUTANTS = {
+    "drop_scale": ("const double sc = p->scale * dot;", "const double sc = dot;"),
+    "exp_sign": ("const double w = exp(sbuf[e] - m);", "const double w = exp(m - sbuf[e]);"),
+    "band_off_by_one": ("if (abs(t / bsize - s / bsize) > radius)",
+                        "if (abs(t / bsize - s / bsize) >= radius)"),
+    "causal_strict": ("if (causal && s > t)\n        return 0;\n    return 1;",
+                      "if (causal && s >= t)\n        return 0;\n    return 1;"),
+    "key_length": ("if (t < 0 || t >= len || s < 0 || s >= len)",
+                   "if (t < 0 || t >= len || s < 0 || s > len)"),
+    "values_from_keys": ("const float *vs = p->v + (base + sidx[e]) * d;",
+                         "const float *vs = p->k + (base + sidx[e]) * d;"),
+    "query_from_key": ("const float *qt = p->q + (base + t) * d;",
+                       "const float *qt = p->k + (base + t) * d;"),
+    "no_normalise": ("        o_row[c] /= l;\n", "        o_row[c] /= 1.0;\n"),
+    "lse_drops_max": ("*lse = m + log(l);", "*lse = log(l);"),
+    "floor_blocks": ("return (len + bsize - 1) / bsize;", "return len / bsize;"),
+    "causal_blocks": ("if (causal && j > i)", "if (causal && j >= i)"),
+    "list_drops_last": ("j <= i + radius; ++j)\n                if (block_in_band",
+                        "j < i + radius; ++j)\n                if (block_in_band"),
+    "recurrence_no_correction": ("acc[e] *= corr;", "acc[e] *= 1.0;"),
+    "recurrence_den": ("den = den * corr + add;", "den = den + add;"),
+    "window_hi": ("int s_hi = (ib + p->radius + 1) * p->bsize; /* exclusive */",
+                  "int s_hi = (ib + p->radius) * p->bsize; /* exclusive */"),
+}
+
+
+def _battery(lib):
+    """Run the pins; return the names of those that fail."""
+    failed = []
+    rng = np.random.default_rng(2024)
+    cases = [(32, 6, 1, False, [192, 150]), (32, 6, 2, True, [192, 70]),
+             (4, 10, 3, False, [40, 17]), (8, 5, 0, True, [40, 33])]
+    for bsize, nblk, radius, causal, lens in cases:
+        n = nblk * bsize
+        lens = np.array(lens, dtype=np.int32)
+        q, k, v = [(rng.standard_normal((2, 2, n, 8))).astype(np.float32) for _ in range(3)]
+        try:
+            o, lse, psum = oracle.forward(q, k, v, lens, bsize, radius, causal, lib=lib)
+            ro, rl = dense_reference(q, k, v, lens, bsize, radius, causal)
+            if not np.max(np.abs(o - ro)) <= 1e-12:
+                failed.append("brute_force_o")
+            for b in range(2):
+                L = lens[b]
+                if not np.allclose(lse[b, :, :L], rl[b, :, :L], rtol=0, atol=1e-12):
+                    failed.append("brute_force_lse")
+                if not np.allclose(psum[b, :, :L], 1.0, atol=1e-13):
+                    failed.append("psum")
+            r = oracle.forward_recurrence(q, k, v, lens, bsize, radius, causal, lib=lib)
+            if not np.max(np.abs(r - ro)) <= 1e-12:
+                failed.append("recurrence")
+            act = oracle.active_blocks(2, n, bsize, radius, causal, lens, lib=lib)
+            msk = oracle.masks(2, n, bsize, radius, causal, lens, act, lib=lib)
+            for b in range(2):
+                keep = token_mask(n, int(lens[b]), bsize, radius, causal)
+                for i in range(nblk):
+                    rows = keep[i * bsize:(i + 1) * bsize]
+                    ref = [j for j in range(nblk) if rows[:, j * bsize:(j + 1) * bsize].any()]
+                    if [int(j) for j in act[b, i] if j >= 0] != ref:
+                        failed.append("lists")
+                    for slot, j in enumerate(act[b, i]):
+                        if j < 0:
+                            continue
+                        blk = rows[:, j * bsize:(j + 1) * bsize]
+                        words = [sum(1 << c for c in range(bsize) if blk[rr, c])
+                                 for rr in range(bsize)]
+                        if list(msk[b, i, slot]) != words:
+                            failed.append("masks")
+        except oracle.OracleError:
+            failed.append("error")
+    return sorted(set(failed))
+
+
+def test_unmodified_oracle_passes_battery():
+    assert _battery(oracle.load()) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    old, new = MUTANTS[name]
+    with open(obuild.SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "orc_mutant.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        lib_path = obuild.build(out=os.path.join(tmp, "liborc_mutant.so"), src=path)
+        lib = oracle.load(lib_path)
+        assert _battery(lib) != [], f"mutant {name} slipped through every pin"
