@@ -1,0 +1,190 @@
+"""ctypes binding of libbsl.so (include/bsl.h), same names as the C ABI.
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the hipStream_t, statuses become exceptions.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback, and using
+the binding without the built library raises ``BslError``.
+
+    plan = bsl_create(BslDesc(head_dim=64, heads=8, radius=2))
+    bsl_forward(plan, batch, n, q, k, v, o, seqlens, None)
+    bsl_destroy(plan)
+
+or, with shape checks on torch tensors, ``Plan(...).forward(q, k, v, seqlens)``.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbsl.so")
+
+BSL_OK, BSL_E_INVALID, BSL_E_UNSUPPORTED, BSL_E_DEVICE, BSL_E_NOMEM = range(5)
+BSL_BF16, BSL_F32 = 0, 1
+
+# every function include/bsl.h declares
+EXPORTS = ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_destroy",
+           "bsl_status_string", "bsl_last_error", "bsl_version")
+
+
+class BslError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+class BslDesc(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("radius", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+    def __init__(self, head_dim=64, heads=1, radius=1, causal=False, dtype=BSL_BF16, scale=0.0,
+                 block_size=32):
+        super().__init__(head_dim, heads, block_size, radius, int(causal), dtype, scale)
+
+
+_lib = None
+
+
+def load(path=LIB_PATH):
+    """The loaded library (loads it on first use)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise BslError(BSL_E_UNSUPPORTED,
+                       f"{path} is not built; run `python -m block_sparse_local_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.bsl_create.argtypes = [ctypes.POINTER(BslDesc), ctypes.POINTER(vp)]
+    lib.bsl_forward.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.bsl_forward_traced.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.bsl_destroy.argtypes = [vp]
+    lib.bsl_status_string.argtypes = [ctypes.c_int]
+    lib.bsl_status_string.restype = ctypes.c_char_p
+    lib.bsl_last_error.argtypes = []
+    lib.bsl_last_error.restype = ctypes.c_char_p
+    lib.bsl_version.argtypes = []
+    lib.bsl_version.restype = i32
+    for name in ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_destroy"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != BSL_OK:
+        lib = load()
+        raise BslError(status, f"{lib.bsl_status_string(status).decode()}: "
+                               f"{lib.bsl_last_error().decode()}")
+
+
+def _ptr(x):
+    """torch tensor -> device address; int -> itself; None -> NULL."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+# ------------------------------------------------------------- raw C names
+
+def bsl_create(desc):
+    plan = ctypes.c_void_p()
+    _check(load().bsl_create(ctypes.byref(desc), ctypes.byref(plan)))
+    return plan
+
+
+def bsl_forward(plan, batch, n, q, k, v, o, seqlens=None, lse=None, stream=None):
+    _check(load().bsl_forward(plan, batch, n, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seqlens),
+                              _ptr(lse), _stream(stream)))
+
+
+def bsl_forward_traced(plan, batch, n, q, k, v, o, seqlens, lse, active, masks, stream=None):
+    _check(load().bsl_forward_traced(plan, batch, n, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                     _ptr(seqlens), _ptr(lse), _ptr(active), _ptr(masks),
+                                     _stream(stream)))
+
+
+def bsl_destroy(plan):
+    _check(load().bsl_destroy(plan))
+
+
+def bsl_status_string(status):
+    return load().bsl_status_string(status).decode()
+
+
+def bsl_last_error():
+    return load().bsl_last_error().decode()
+
+
+def bsl_version():
+    return load().bsl_version()
+
+
+# ------------------------------------------------------ torch convenience
+
+class Plan:
+    """A plan plus shape/dtype checks for torch tensors on the current GPU."""
+
+    def __init__(self, head_dim, heads, radius, causal=False, dtype="bf16", scale=0.0):
+        self.head_dim, self.heads, self.radius, self.causal = head_dim, heads, radius, causal
+        self.dtype = dtype
+        code = {"bf16": BSL_BF16, "f32": BSL_F32}[dtype]
+        self.handle = bsl_create(BslDesc(head_dim, heads, radius, causal, code, scale))
+
+    def close(self):
+        if self.handle is not None:
+            bsl_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check_tensors(self, q, k, v, o, seqlens, lse):
+        import torch
+        tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[self.dtype]
+        if q.dim() != 4 or q.shape[1] != self.heads or q.shape[3] != self.head_dim:
+            raise ValueError(f"q must be [batch, {self.heads}, n, {self.head_dim}]")
+        for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+            if t.shape != q.shape or t.dtype != tdt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {tdt} CUDA tensor of shape "
+                                 f"{tuple(q.shape)}")
+        if seqlens is not None and (seqlens.dtype != torch.int32 or not seqlens.is_cuda
+                                    or seqlens.shape != (q.shape[0],)):
+            raise ValueError("seqlens must be an int32 CUDA tensor of shape [batch]")
+        if lse is not None and (lse.dtype != torch.float32 or lse.shape != q.shape[:3]
+                                or not lse.is_contiguous()):
+            raise ValueError("lse must be a contiguous float32 tensor of shape [batch, heads, n]")
+
+    def forward(self, q, k, v, seqlens=None, o=None, lse=None, stream=None):
+        import torch
+        if o is None:
+            o = torch.empty_like(q)
+        self._check_tensors(q, k, v, o, seqlens, lse)
+        bsl_forward(self.handle, q.shape[0], q.shape[2], q, k, v, o, seqlens, lse, stream)
+        return o
+
+    def forward_traced(self, q, k, v, seqlens=None, o=None, lse=None, stream=None):
+        """Returns (o, active, masks); see bsl_forward_traced in include/bsl.h."""
+        import torch
+        if o is None:
+            o = torch.empty_like(q)
+        self._check_tensors(q, k, v, o, seqlens, lse)
+        batch, n = q.shape[0], q.shape[2]
+        w = 2 * self.radius + 1
+        active = torch.empty((batch, n // 32, w), dtype=torch.int32, device=q.device)
+        masks = torch.empty((batch, n // 32, w, 32), dtype=torch.int32, device=q.device)
+        bsl_forward_traced(self.handle, batch, n, q, k, v, o, seqlens, lse, active, masks, stream)
+        return o, active, masks

@@ -1,0 +1,190 @@
+// bsl_api.cpp -- the C ABI declared in include/bsl.h: argument checks, device
+// checks, dispatch to the kernel launchers.  No allocation on the device, no
+// synchronisation, nothing thrown across the interface.
+#include "bsl.h"
+
+#include "launch.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+struct bsl_plan {
+    bsl_desc desc;
+    float scale;  // resolved
+    int device;   // HIP ordinal the plan was made on
+    int cu_count; // compute units of that device
+};
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+bsl_status fail(bsl_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+
+bsl_status fail(bsl_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bsl_status run(const bsl_plan *plan, int32_t batch, int32_t n, const void *q, const void *k,
+               const void *v, void *o, const int32_t *seqlens, float *lse, int32_t *active,
+               uint32_t *masks, void *stream, bool traced)
+{
+    if (!plan)
+        return fail(BSL_E_INVALID, "plan is NULL");
+    const bsl_desc &d = plan->desc;
+    if (batch < 0 || n < 0)
+        return fail(BSL_E_INVALID, "batch (%d) and n (%d) must be >= 0", batch, n);
+    if (n % d.block_size != 0)
+        return fail(BSL_E_INVALID, "n (%d) is not a multiple of the block size %d", n,
+                    d.block_size);
+    if (batch == 0 || n == 0)
+        return BSL_OK;
+    if (!q || !k || !v || !o)
+        return fail(BSL_E_INVALID, "q, k, v and o must be non-NULL device pointers");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(BSL_E_INVALID, "q, k, v and o must be 16-byte aligned");
+    if (traced && (!active || !masks))
+        return fail(BSL_E_INVALID, "traced forward needs non-NULL active and masks");
+    // element counts must fit comfortably in 64-bit offsets, grids in 31 bits
+    const long double elems = (long double)batch * d.heads * (long double)n * d.head_dim;
+    if (elems > 9.0e18L)
+        return fail(BSL_E_INVALID, "tensor of %d x %d x %d x %d elements is too large", batch,
+                    d.heads, n, d.head_dim);
+    const long long nblk = n / d.block_size;
+    if ((long long)batch * d.heads * nblk > 0x7fffffffLL)
+        return fail(BSL_E_INVALID, "batch * heads * n / 32 exceeds 2^31 - 1");
+    const uint8_t *ob = (const uint8_t *)o;
+    const size_t esz = d.dtype == BSL_BF16 ? 2 : 4;
+    const size_t bytes = (size_t)elems * esz;
+    for (const void *in : {q, k, v}) {
+        const uint8_t *ib = (const uint8_t *)in;
+        if (ib < ob + bytes && ob < ib + bytes)
+            return fail(BSL_E_INVALID, "o overlaps one of q, k, v");
+    }
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return fail(BSL_E_DEVICE, "hipGetDevice failed");
+    if (dev != plan->device)
+        return fail(BSL_E_INVALID, "current device %d is not the plan's device %d", dev,
+                    plan->device);
+
+    bsl::Launch a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.seqlens = seqlens;
+    a.lse = lse;
+    a.active = traced ? active : nullptr;
+    a.masks = traced ? masks : nullptr;
+    a.batch = batch;
+    a.heads = d.heads;
+    a.n = n;
+    a.head_dim = d.head_dim;
+    a.radius = d.radius;
+    a.causal = d.causal != 0;
+    a.scale = plan->scale;
+    a.stream = (hipStream_t)stream;
+    const hipError_t e = d.dtype == BSL_BF16 ? bsl::launch_fwd_bf16(a) : bsl::launch_fwd_f32(a);
+    if (e != hipSuccess)
+        return fail(BSL_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    return BSL_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+bsl_status bsl_create(const bsl_desc *desc, bsl_plan **plan)
+{
+    if (!desc || !plan)
+        return fail(BSL_E_INVALID, "desc and plan must be non-NULL");
+    *plan = nullptr;
+    const bsl_desc &d = *desc;
+    if (d.heads < 1)
+        return fail(BSL_E_INVALID, "heads must be >= 1 (got %d)", d.heads);
+    if (d.radius < 0)
+        return fail(BSL_E_INVALID, "radius must be >= 0 (got %d)", d.radius);
+    if (d.causal != 0 && d.causal != 1)
+        return fail(BSL_E_INVALID, "causal must be 0 or 1 (got %d)", d.causal);
+    if (!std::isfinite(d.scale))
+        return fail(BSL_E_INVALID, "scale must be finite");
+    if (d.block_size != 32)
+        return fail(BSL_E_UNSUPPORTED, "block_size must be 32 (got %d)", d.block_size);
+    if (d.head_dim != 32 && d.head_dim != 64 && d.head_dim != 128)
+        return fail(BSL_E_UNSUPPORTED, "head_dim must be 32, 64 or 128 (got %d)", d.head_dim);
+    if (d.dtype != BSL_BF16 && d.dtype != BSL_F32)
+        return fail(BSL_E_UNSUPPORTED, "unknown dtype %d", d.dtype);
+    if (d.radius > (1 << 24))
+        return fail(BSL_E_UNSUPPORTED, "radius %d is too large", d.radius);
+
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return fail(BSL_E_DEVICE, "no HIP device");
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return fail(BSL_E_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(BSL_E_UNSUPPORTED, "device %d is %s; this library is built for gfx950", dev,
+                    prop.gcnArchName);
+
+    bsl_plan *p = new (std::nothrow) bsl_plan;
+    if (!p)
+        return fail(BSL_E_NOMEM, "out of host memory");
+    p->desc = d;
+    p->scale = d.scale > 0.0f ? d.scale : 1.0f / std::sqrt((float)d.head_dim);
+    p->device = dev;
+    p->cu_count = prop.multiProcessorCount;
+    *plan = p;
+    return BSL_OK;
+}
+
+bsl_status bsl_forward(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
+                       const void *k, const void *v, void *o, const int32_t *seqlens,
+                       float *lse, void *stream)
+{
+    return run(plan, batch, n, q, k, v, o, seqlens, lse, nullptr, nullptr, stream, false);
+}
+
+bsl_status bsl_forward_traced(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
+                              const void *k, const void *v, void *o, const int32_t *seqlens,
+                              float *lse, int32_t *active, uint32_t *masks, void *stream)
+{
+    return run(plan, batch, n, q, k, v, o, seqlens, lse, active, masks, stream, true);
+}
+
+bsl_status bsl_destroy(bsl_plan *plan)
+{
+    delete plan;
+    return BSL_OK;
+}
+
+const char *bsl_status_string(bsl_status s)
+{
+    switch (s) {
+    case BSL_OK: return "BSL_OK";
+    case BSL_E_INVALID: return "BSL_E_INVALID: invalid argument";
+    case BSL_E_UNSUPPORTED: return "BSL_E_UNSUPPORTED: not supported by this build or device";
+    case BSL_E_DEVICE: return "BSL_E_DEVICE: HIP runtime error";
+    case BSL_E_NOMEM: return "BSL_E_NOMEM: out of host memory";
+    }
+    return "unknown bsl_status";
+}
+
+const char *bsl_last_error(void) { return g_last_error; }
+
+int32_t bsl_version(void) { return BSL_VERSION; }
+
+} // extern "C"

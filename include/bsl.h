@@ -1,0 +1,130 @@
+/*
+ * bsl.h -- C ABI of libbsl.so: banded block-sparse attention forward on
+ * MI355X (gfx950).
+ *
+ * The operation is the forward pass described on the NucleoByte project page
+ * ("NucleoByte: GPU-Accelerated Block-Sparse Genomic Language Model"):
+ *   - section 3, "Localized Block-Sparse Attention Matrix": with block size
+ *     B = 32, query block i attends only to key blocks j with |i - j| <= R;
+ *   - section 3, "Softmax Normalization & Online Numerical Stability": scores
+ *     S = Q K^T / sqrt(d_k); a running row maximum, denominator and output are
+ *     carried across the active key blocks, and the output is the softmax-
+ *     weighted sum of V (divided by the denominator after the last block);
+ *   - section 2, item 2, "Dynamic Ceiling Hardware Alignment": each batch is
+ *     padded up to a multiple of 32; keys past a sequence's own length are
+ *     masked, and blocks that hold only padding are skipped.
+ * An optional causal flag additionally drops keys after the query (s > t).
+ *
+ * Layout.  Q, K, V and O are dense [batch][heads][n][head_dim] arrays, head_dim
+ * innermost, in the plan's dtype (bf16 or fp32), on the device the plan was
+ * created on.  n is the padded buffer length (a multiple of 32).  Row t of a
+ * sequence with length L is real when t < L; rows t >= L are padding: their
+ * Q/K/V values are never used (they may hold NaN) and their O rows are written
+ * as zeros.
+ *
+ * Ownership.  The caller owns every buffer.  A plan holds only immutable
+ * settings and device facts; it allocates no device memory, so one plan may be
+ * used from several host threads and streams at once.
+ *
+ * Asynchrony.  bsl_forward and bsl_forward_traced only enqueue work on the
+ * given stream (NULL = the default stream) and never synchronise.
+ *
+ * Errors.  Every call returns a bsl_status.  Argument errors are reported
+ * before anything is launched, and then nothing is written.  A failed launch
+ * returns BSL_E_DEVICE.  bsl_last_error() gives a per-thread text for the last
+ * failing call.  Nothing aborts, exits or throws across this interface.
+ */
+#ifndef BSL_H
+#define BSL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSL_VERSION 10000 /* major * 10000 + minor * 100 + patch */
+
+typedef enum bsl_status {
+    BSL_OK = 0,
+    BSL_E_INVALID = 1,     /* bad argument: nothing was launched or written */
+    BSL_E_UNSUPPORTED = 2, /* well-formed but outside what this build supports */
+    BSL_E_DEVICE = 3,      /* HIP runtime failure (device query or launch) */
+    BSL_E_NOMEM = 4        /* host allocation of a plan failed */
+} bsl_status;
+
+typedef enum bsl_dtype {
+    BSL_BF16 = 0, /* bf16 in and out; bf16 MFMA products, fp32 accumulation */
+    BSL_F32 = 1   /* fp32 in and out; fp32 arithmetic throughout */
+} bsl_dtype;
+
+typedef struct bsl_desc {
+    int32_t head_dim;   /* d: 32, 64 or 128 */
+    int32_t heads;      /* heads per sequence, >= 1 */
+    int32_t block_size; /* B: must be 32, the block size the page fixes */
+    int32_t radius;     /* R >= 0: key blocks j with |i - j| <= R are scored */
+    int32_t causal;     /* 0 or 1: 1 also drops keys s > t */
+    int32_t dtype;      /* a bsl_dtype */
+    float scale;        /* > 0: score scale; <= 0: 1 / sqrt(head_dim) */
+} bsl_desc;
+
+typedef struct bsl_plan bsl_plan;
+
+/* Validate *desc against the current HIP device and make a plan for it.
+ * BSL_E_INVALID: desc or plan NULL, heads < 1, radius < 0, causal not 0/1,
+ *   non-finite scale.
+ * BSL_E_UNSUPPORTED: head_dim not 32/64/128, block_size != 32, unknown dtype,
+ *   or the current device is not gfx950.
+ * BSL_E_DEVICE: the device could not be queried.
+ * On success *plan is set; release it with bsl_destroy. */
+bsl_status bsl_create(const bsl_desc *desc, bsl_plan **plan);
+
+/* Enqueue the forward pass.
+ *   batch   >= 0 sequences; n >= 0 rows per sequence buffer, n % 32 == 0.
+ *           batch == 0 or n == 0 is a no-op returning BSL_OK.
+ *   q, k, v device pointers, [batch][heads][n][head_dim] in the plan's dtype.
+ *   o       device pointer, same shape and dtype; every row is written.  It must
+ *           not overlap q, k or v.
+ *   seqlens device int32[batch] with 0 <= seqlens[b] <= n, or NULL for all n.
+ *           Values outside [0, n] are clamped to it on the device.
+ *   lse     device float[batch][heads][n] or NULL: natural-log log-sum-exp of
+ *           each row's scaled scores over its kept keys; -inf on padded rows.
+ *   stream  a hipStream_t, or NULL for the default stream.
+ * Returns BSL_E_INVALID for a NULL plan, negative sizes, n % 32 != 0, a NULL
+ * q/k/v/o when batch * n > 0, or sizes whose element count does not fit in 63
+ * bits; BSL_E_INVALID also when the current device is not the plan's. */
+bsl_status bsl_forward(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
+                       const void *k, const void *v, void *o, const int32_t *seqlens,
+                       float *lse, void *stream);
+
+/* bsl_forward, plus a record of what the kernel did, for verification:
+ *   active  device int32[batch][n/32][2R+1]: for query block i of sequence b,
+ *           the key blocks the kernel visited, ascending, then -1 in the unused
+ *           slots (all -1 for blocks that hold only padding).
+ *   masks   device uint32[batch][n/32][2R+1][32]: for slot s of query block i,
+ *           word r has bit c set iff the kernel kept key c of that key block
+ *           for query row r; zero for unused slots and padded query rows.
+ * Both are required (non-NULL) and are written in full; they describe head 0
+ * (the band and the masks are the same for every head). */
+bsl_status bsl_forward_traced(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
+                              const void *k, const void *v, void *o, const int32_t *seqlens,
+                              float *lse, int32_t *active, uint32_t *masks, void *stream);
+
+/* Release a plan.  NULL is accepted and ignored.  Do not call while work
+ * enqueued with the plan is being launched from another thread. */
+bsl_status bsl_destroy(bsl_plan *plan);
+
+/* Static text for a status code. */
+const char *bsl_status_string(bsl_status status);
+
+/* Text describing the last failing call on this host thread ("" if none). */
+const char *bsl_last_error(void);
+
+/* BSL_VERSION of the library actually loaded. */
+int32_t bsl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSL_H */

@@ -1,0 +1,89 @@
+"""The C-ABI library on the CPU: it loads, exports what include/bsl.h declares,
+and rejects bad arguments before touching a device.  No compute call here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_sparse_local_amd import bsl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsl.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bsl.LIB_PATH):
+        from block_sparse_local_amd import build
+        build.build()
+    return bsl.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsl_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(bsl.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", bsl.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (\w+)", out))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_version_matches_header(lib):
+    m = re.search(r"#define BSL_VERSION (\d+)", open(HEADER).read())
+    assert bsl.bsl_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert bsl.bsl_status_string(code).startswith("BSL_")
+    assert "unknown" in bsl.bsl_status_string(99)
+
+
+def _create_status(lib, **kw):
+    desc = bsl.BslDesc(**kw)
+    plan = ctypes.c_void_p()
+    return lib.bsl_create(ctypes.byref(desc), ctypes.byref(plan)), plan
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads=0), bsl.BSL_E_INVALID),
+    (dict(radius=-1), bsl.BSL_E_INVALID),
+    (dict(causal=2), bsl.BSL_E_INVALID),
+    (dict(scale=float("nan")), bsl.BSL_E_INVALID),
+    (dict(block_size=16), bsl.BSL_E_UNSUPPORTED),
+    (dict(head_dim=48), bsl.BSL_E_UNSUPPORTED),
+    (dict(head_dim=256), bsl.BSL_E_UNSUPPORTED),
+    (dict(dtype=7), bsl.BSL_E_UNSUPPORTED),
+])
+def test_create_rejects_bad_descriptors_before_device_use(lib, kw, status):
+    st, plan = _create_status(lib, **kw)
+    assert st == status
+    assert plan.value is None
+    assert bsl.bsl_last_error() != ""
+
+
+def test_null_arguments(lib):
+    assert lib.bsl_create(None, None) == bsl.BSL_E_INVALID
+    assert lib.bsl_forward(None, 1, 32, 16, 16, 16, 16, None, None, None) == bsl.BSL_E_INVALID
+    assert "plan" in bsl.bsl_last_error()
+    assert lib.bsl_forward_traced(None, 1, 32, 16, 16, 16, 16, None, None, 16, 16,
+                                  None) == bsl.BSL_E_INVALID
+    assert lib.bsl_destroy(None) == bsl.BSL_OK
+
+
+def test_binding_raises_on_error(lib):
+    with pytest.raises(bsl.BslError) as e:
+        bsl.bsl_create(bsl.BslDesc(head_dim=48))
+    assert e.value.status == bsl.BSL_E_UNSUPPORTED
