@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark: banded block-sparse attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c4|c5|c3|c2|c1]
+
+One step is one forward call of the whole hot path (block plan, Q/K/V loads,
+scores, masks, online softmax, P V, normalisation and store) over one batch of
+seeded synthetic inputs already resident in HBM.  W untimed steps, then K timed
+steps between two device synchronisations.  Prints one JSON line:
+
+  value        useful TFLOP/s (4 * d per kept query/key pair) over the timed
+               region's wall clock
+  roofline     the kernel's algorithmic bytes (or FLOP) per launch over its
+               mean launch time from HIP events on the launch stream, against
+               the MI355X peak; traffic = HBM bytes per launch measured with
+               rocprofv3 counters (profiles/), null when the kernel source has
+               changed since
+  cpu_baseline the fp64 oracle, as written, timed on this host's cores over a
+               bounded sample of query blocks of the same workload
+
+The default workload is the 1.3B-shape long-context case: batch 1, 16 heads,
+131072-row buffer holding a 130000-token sequence, head dim 128, radius 8.
+``--secondary`` also times the million-token case in the same run.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+KERNEL_SOURCES = ["block_sparse_local_amd/csrc/fwd_bf16.hip", "block_sparse_local_amd/csrc/launch.h"]
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload_key):
+    """Bytes per launch from the committed counter summary, if it was taken on
+    the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"pmc_traffic_fwd_bf16_{workload_key}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"^kernel_source_sha256_16:\s*(\w+)", text, re.M)
+    val = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not sha or not val or sha.group(1) != kernel_sha():
+        return None
+    return float(val.group(1))
+
+
+def to_device(x, dtype):
+    import torch
+    from block_sparse_local_amd import inputs
+    if dtype == "bf16":
+        return torch.from_numpy(inputs.bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+def time_workload(key, steps, warmup, cold=False, log=print):
+    import torch
+    from block_sparse_local_amd import bsl, inputs, workload
+
+    t0 = time.time()
+    d = inputs.make(key, 42)
+    w = d["workload"]
+    lens = d["seqlens"]
+    log(f"[bench] {key} inputs drawn in {time.time() - t0:.1f}s: {w.describe()}")
+    q, k, v = (to_device(d[x], w.dtype) for x in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    sl = torch.from_numpy(lens).cuda()
+    plan = bsl.Plan(w.d, w.heads, w.radius, w.causal, w.dtype)
+    acc = workload.account(lens, w.heads, w.d, w.radius, w.causal, w.dtype)
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if cold else None
+
+    for _ in range(warmup):
+        plan.forward(q, k, v, sl, o=o, stream=stream)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_begin = time.perf_counter()
+    for s in range(steps):
+        if flush is not None:
+            flush.fill_(float(s))
+        starts[s].record(stream)
+        plan.forward(q, k, v, sl, o=o, stream=stream)
+        ends[s].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_begin
+    per_launch = np.array([a.elapsed_time(b) * 1e-3 for a, b in zip(starts, ends)])
+    plan.close()
+    del q, k, v, o, flush
+    torch.cuda.empty_cache()
+    return dict(key=key, w=w, d=d, acc=acc, wall=wall, per_launch=per_launch, steps=steps)
+
+
+def cpu_baseline(r, target_flops=1.5e11, log=print):
+    """Time the fp64 oracle on a bounded, evenly spread sample of query blocks
+    (every head) of the same workload, on this host's cores."""
+    import oracle
+    from block_sparse_local_amd import workload
+    d, w = r["d"], r["w"]
+    lens = d["seqlens"]
+    n = d["n"]
+    nblk = n // 32
+    per_block = r["acc"]["useful_flops"] / max(1, sum(-(-int(L) // 32) for L in lens) * w.heads)
+    want = int(max(1, min(nblk * w.batch, target_flops / max(per_block, 1.0) / w.heads)))
+    sel = []
+    for b in range(w.batch):
+        nb = -(-int(lens[b]) // 32)
+        if nb == 0:
+            continue
+        share = max(1, int(round(want * nb / max(1, sum(-(-int(L) // 32) for L in lens)))))
+        for i in np.unique(np.linspace(0, nb - 1, min(share, nb)).astype(int)):
+            for h in range(w.heads):
+                sel.append((b, h, int(i)))
+    sel = np.array(sel, dtype=np.int32)
+    threads = min(16, oracle.default_threads())
+    t0 = time.perf_counter()
+    oracle.forward_blocks(d["q"], d["k"], d["v"], sel, lens, 32, w.radius, w.causal,
+                          nthreads=threads)
+    dt = time.perf_counter() - t0
+    # useful work of exactly the sampled query rows
+    flops = 0.0
+    tokens = 0
+    for b in range(w.batch):
+        rows = sel[sel[:, 0] == b]
+        if len(rows) == 0:
+            continue
+        L = int(lens[b])
+        for i in np.unique(rows[:, 2]):
+            hcount = int((rows[:, 2] == i).sum())
+            t = np.arange(i * 32, min(L, i * 32 + 32))
+            lo = np.maximum(0, (t // 32 - w.radius) * 32)
+            hi = np.minimum(L, (t // 32 + w.radius + 1) * 32)
+            if w.causal:
+                hi = np.minimum(hi, t + 1)
+            flops += 4.0 * w.d * float((hi - lo).sum()) * hcount
+            tokens += len(t) * hcount
+    log(f"[bench] oracle: {len(sel)} (sequence, head, query block) units in {dt:.1f}s "
+        f"on {threads} threads")
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(sel)} query blocks (of {w.batch * nblk * w.heads} block-heads): "
+                      f"{len(sel) // w.heads} evenly spaced blocks x all {w.heads} heads; "
+                      f"{flops / 1e9:.1f} useful GFLOP in {dt:.2f}s",
+            "tokens_per_s": tokens / w.heads / dt,
+            "seconds": dt}
+
+
+def summarize(r, traffic=None):
+    acc, w = r["acc"], r["w"]
+    t_step = r["wall"] / r["steps"]
+    mean_launch = float(r["per_launch"].mean())
+    alg_bytes, flops = acc["alg_bytes"], acc["useful_flops"]
+    bound = acc["bound"]
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": alg_bytes / mean_launch / 1e9, "peak": 8000.0,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / mean_launch / 1e12,
+                "peak": acc["flops_peak"] / 1e12, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic
+    extra = {
+        "useful_tflops": flops / t_step / 1e12,
+        "tokens_per_s": acc["tokens"] / t_step,
+        "mean_launch_us": mean_launch * 1e6,
+        "median_launch_us": float(np.median(r["per_launch"])) * 1e6,
+        "min_launch_us": float(r["per_launch"].min()) * 1e6,
+        "alg_bytes": alg_bytes,
+        "useful_flops": flops,
+        "computed_flops": acc["computed_flops"],
+        "useful_pairs": acc["useful_pairs"],
+        "block_pairs": acc["block_pairs"],
+        "hbm_frac": alg_bytes / mean_launch / 8.0e12,
+        "mfma_frac": flops / mean_launch / acc["flops_peak"],
+        "roofline_frac": max(acc["t_hbm"], acc["t_mfma"]) / mean_launch,
+    }
+    return t_step, roof, extra
+
+
+def config_of(r):
+    w, d = r["w"], r["d"]
+    return {"workload": f"{w.key} {w.describe()}", "batch": w.batch, "heads": w.heads,
+            "n": int(d["n"]), "head_dim": w.d, "radius": w.radius, "causal": w.causal,
+            "block_size": 32, "tokens": int(np.sum(d["seqlens"])),
+            "seqlens": [int(x) for x in d["seqlens"]] if w.batch <= 8 else "ragged"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--secondary", action="store_true",
+                    help="also time the million-token workload (c5)")
+    ap.add_argument("--cold", action="store_true",
+                    help="overwrite 1 GiB between steps (outside the events)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 1 GiB device copies (for counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the banded attention forward is not sharded across "
+              "GPUs in this library (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    import torch
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(max(1, args.steps)):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {a.numel() * 4} bytes x {max(1, args.steps)}")
+        return
+
+    r = time_workload(args.workload, args.steps, args.warmup, args.cold, log)
+    traffic = stored_traffic(args.workload) if r["w"].dtype == "bf16" else None
+    t_step, roof, extra = summarize(r, traffic)
+    log(f"[bench] {args.workload}: {t_step * 1e3:.3f} ms/step, {extra['useful_tflops']:.1f} "
+        f"useful TFLOP/s, {roof['achieved']:.0f} {roof['unit']} ({roof['frac'] * 100:.1f}% of "
+        f"{roof['bound']} peak)")
+
+    line = {
+        "metric": "block-sparse attn fwd useful TFLOP/s (+ tokens/s, % of bf16 MFMA/HBM roofline)",
+        "value": extra["useful_tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": r["w"].dtype,
+        "data": "synthetic: seeded N(0,1) Q/K/V rounded to bf16 (no dataset)",
+        "config": config_of(r),
+        "tokens_per_s": extra["tokens_per_s"],
+        "roofline": roof,
+        "detail": extra,
+    }
+    if args.cold:
+        line["timing"] = "cold: 1 GiB overwritten between steps"
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(r, log=log)
+    del r
+    if args.secondary and args.workload != "c5":
+        r5 = time_workload("c5", args.steps, args.warmup, args.cold, log)
+        t5, roof5, extra5 = summarize(r5, stored_traffic("c5"))
+        line["secondary"] = {"config": config_of(r5), "ms_per_step": t5 * 1e3,
+                             "value": extra5["useful_tflops"], "unit": "TFLOP/s",
+                             "tokens_per_s": extra5["tokens_per_s"], "roofline": roof5,
+                             "detail": extra5}
+        log(f"[bench] c5: {t5 * 1e3:.3f} ms/step, {roof5['achieved']:.0f} {roof5['unit']} "
+            f"({roof5['frac'] * 100:.1f}%)")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,7 +22,10 @@ SOURCES = ["fwd_bf16.hip", "fwd_f32.hip", "bsl_api.cpp"]
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
-DEVICE_ONLY = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# no packed-fp32 instruction selection; MFMA accumulators in ordinary VGPRs
+# (the AGPR form makes the compiler copy every accumulator each step)
+DEVICE_ONLY = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src, obj, extra=()):

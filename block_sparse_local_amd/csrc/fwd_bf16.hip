@@ -14,22 +14,28 @@
 //  * One workgroup = MQ waves = MQ consecutive query blocks of one (batch, head).
 //    The workgroup sweeps the union of their bands, one key block per step; each
 //    K/V block is brought into LDS once and serves every wave whose band covers
-//    it (up to 2R+1 of them).  Two LDS buffers: block j+1 is fetched from HBM
-//    into registers while block j is computed, then written to the other buffer.
+//    it (up to 2R+1 of them).
+//  * K and V blocks travel HBM -> LDS with direct-to-LDS loads (no registers),
+//    into a ring of NSTAGE buffers filled NSTAGE-1 blocks ahead of use; one
+//    barrier per step both publishes the oldest block and frees the buffer the
+//    previous step read.  16-byte chunks are XOR-swizzled per row so that the
+//    MFMA operand reads below hit distinct LDS banks.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    in the 32x32 accumulator each lane then owns one query (column) and 16 of
 //    the 32 keys, so the row maximum is 15 in-register max ops plus one exchange
 //    with the lane 32 away, and m, l and the rescale factor stay per lane.
-//  * The output is also formed transposed, O^T += V^T P^T, so P^T is used as the
-//    MFMA B operand straight from the score accumulator (rounded to bf16); the
-//    key order inside the contraction is permuted to match the accumulator's
-//    register order, and V is written into LDS transposed in that same order.
+//  * The output is also formed transposed, O^T += V^T P^T.  P^T is the MFMA B
+//    operand straight from the score accumulator (rounded to bf16), with the key
+//    order inside each 16-key step permuted to the accumulator's register order;
+//    the matching V^T operand is read from the row-major V tile with the
+//    transposing LDS read (ds_read_b64_tr_b16), four keys at a time.
 //  * exp is the hardware 2^x with log2(e) folded into the score scale.  The
 //    running maximum is only moved when a row's maximum grows by more than 2^8;
 //    O / l is unchanged by the choice of reference point, and p stays <= 256.
 //  * l is summed from the same bf16-rounded probabilities the PV product uses.
-//  * Padded keys of the last block are masked by select (never by a multiply)
-//    and their V rows are zeroed as they enter LDS, so NaN padding cannot leak.
+//  * Padded keys of the last block are masked by select (never by a multiply),
+//    and their V rows are zeroed in LDS once the block has landed, so NaN
+//    padding cannot leak.
 //  * Workgroup ids are remapped so that each XCD (its own L2) works through a
 //    contiguous run of query groups: neighbouring groups share K/V halo blocks.
 #include "launch.h"
@@ -40,11 +46,14 @@ namespace bsl {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int BLK = 32;
 constexpr float LOG2E = 1.4426950408889634f;
@@ -76,42 +85,78 @@ __device__ __forceinline__ int xcd_remap(int g, int total)
 // result: rows 8*(r/4) + 4*half + (r%4).
 __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
-// Position of key kk inside a transposed V row in LDS: bits 2 and 3 swapped, so
-// the 8 keys a lane half needs for one 16-key MFMA step are contiguous.
-__device__ __forceinline__ int vt_pos(int kk)
-{
-    return (kk & ~12) | (((kk >> 2) & 1) << 3) | (((kk >> 3) & 1) << 2);
-}
-
-// Element offset of (dim row, key position) in the transposed V tile: rows of
-// 32 bf16, 16-byte chunks XOR-swizzled by the row to spread LDS banks.
-__device__ __forceinline__ int vt_off(int row, int pos)
-{
-    return row * BLK + ((((pos >> 3) ^ ((row >> 1) & 3))) << 3) + (pos & 7);
-}
+// LDS tile geometry for head dim D: 32 rows of D bf16, row-major, CPR 16-byte
+// chunks per row, chunk c of row r stored at chunk position c ^ swizzle(r).
+template <int D>
+struct Tile {
+    static constexpr int CPR = D / 8;
+    static constexpr int BYTES = BLK * D * 2;
+    static constexpr int ROWS_PER_256B = 16 / CPR;
+    // K is read as 32 rows x one logical chunk: spread 16 consecutive rows over
+    // 16 distinct chunk positions of a 256-byte bank window.
+    __device__ static __forceinline__ int k_swz(int r) { return (r / ROWS_PER_256B) % CPR; }
+    // V is read 4 consecutive rows x 4 consecutive logical chunks at a time
+    // (transposing reads): put the 4 rows in 4 different aligned 4-chunk sets.
+    __device__ static __forceinline__ int v_swz(int r)
+    {
+        return ((r / ROWS_PER_256B) & (CPR / 4 - 1)) << 2;
+    }
+};
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-template <int D, int MQ, bool CAUSAL, bool TRACE>
+// vmcnt(n) together with lgkmcnt(0); expcnt left alone.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void workgroup_barrier()
+{
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+// The V^T operands of one 32-wide output tile: four transposing LDS reads at
+// rows +0, +8, +16, +24 from `addr` (a 32-bit LDS address), waited for inside
+// the same asm block.  The builtin form of this read makes the compiler drain
+// every outstanding direct-to-LDS load first, which would empty the K/V ring on
+// every step; issued here, nothing of these reads is left in flight.
+template <int ROW_BYTES>
+__device__ __forceinline__ void tr_tile(uint32_t addr, u32x2 &a0, u32x2 &a1, u32x2 &a2, u32x2 &a3)
+{
+    __asm__ volatile("ds_read_b64_tr_b16 %0, %4\n\t"
+                     "ds_read_b64_tr_b16 %1, %4 offset:%5\n\t"
+                     "ds_read_b64_tr_b16 %2, %4 offset:%6\n\t"
+                     "ds_read_b64_tr_b16 %3, %4 offset:%7\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
+                     : "v"(addr), "i"(8 * ROW_BYTES), "i"(16 * ROW_BYTES), "i"(24 * ROW_BYTES));
+}
+
+template <int D, int MQ, int NSTAGE, bool CAUSAL, bool TRACE>
 __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
 {
+    using T = Tile<D>;
     constexpr int NT = MQ * 64;
-    constexpr int KROW = D + 8;         // K row pitch in LDS (bf16): 16 bytes of pad
-    constexpr int KSZ = BLK * KROW;     // K tile (bf16 elements)
-    constexpr int VSZ = D * BLK;        // V^T tile: D rows of 32 keys
-    constexpr int BUF = KSZ + VSZ;
-    constexpr int NMT = D / 32;         // 32-wide output tiles
-    constexpr int NKS = D / 16;         // 16-deep steps of the score contraction
-    constexpr int KCH = BLK * D / 8;    // 16-byte chunks in a K block
-    constexpr int KPT = (KCH + NT - 1) / NT;
-    constexpr int VTASK = 16 * (D / 8); // (key pair, 8-dim chunk) tasks per V block
-    constexpr int VPT = (VTASK + NT - 1) / NT;
+    constexpr int NMT = D / 32;                 // 32-wide output tiles
+    constexpr int NKS = D / 16;                 // 16-deep steps of the score contraction
+    constexpr int STAGE = 2 * T::BYTES;         // K tile then V tile
+    constexpr int SLOTS = STAGE / 16;           // 16-byte slots per stage
+    static_assert(SLOTS % NT == 0, "each thread issues the same number of loads");
+    constexpr int LPT = SLOTS / NT;             // direct-to-LDS loads per thread per block
+    static_assert(T::BYTES % (64 * 16) == 0, "a wave's load covers only K or only V");
     static_assert(D % 32 == 0 && D <= 128, "head_dim must be 32, 64 or 128");
+    static_assert(NSTAGE >= 2, "ring depth");
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
 
     const int g = xcd_remap((int)blockIdx.x, p.total);
@@ -166,6 +211,25 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
     if (CAUSAL && jhi > i0 + MQ - 1)
         jhi = i0 + MQ - 1;
 
+    // ------------------------------------------- K/V ring: direct-to-LDS
+    // Slot s of a stage (16 bytes at stage + 16 s) holds K (s < SLOTS/2) or V;
+    // within a tile, slot -> (row, chunk position), chunk position -> logical
+    // chunk through the row's swizzle.  Load u of wave w fills slots
+    // [u*NT + 64w, +64): 1 KB of LDS, 1 KB of contiguous global rows.
+    auto issue = [&](int j, int stage) {
+#pragma unroll
+        for (int u = 0; u < LPT; ++u) {
+            const int s = u * NT + tid;
+            const bool is_v = s >= SLOTS / 2;
+            const int t = is_v ? s - SLOTS / 2 : s;
+            const int r = t / T::CPR, cp = t % T::CPR;
+            const int c = cp ^ (is_v ? T::v_swz(r) : T::k_swz(r));
+            const uint16_t *src = (is_v ? vg : kg) + (size_t)(j * BLK + r) * D + c * 8;
+            uint8_t *dst = lds + stage * STAGE + (u * NT + wave * 64) * 16;
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
+        }
+    };
+
     // ----------------------------------------------------------- Q fragment
     const int qrow = i * BLK + col;
     const bool qvalid = exists && qrow < len;
@@ -178,6 +242,12 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
         qf[s] = as_bf16x8(x);
     }
 
+    // start the ring before waiting on anything
+#pragma unroll
+    for (int a = 0; a < NSTAGE - 1; ++a)
+        if (jlo + a <= jhi)
+            issue(jlo + a, a);
+
     f32x16 oacc[NMT];
 #pragma unroll
     for (int m = 0; m < NMT; ++m)
@@ -187,78 +257,41 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
     float m_used = -INFINITY; // reference maximum (log2 units)
     float lsum = 0.0f;        // this lane's share of the denominator
 
-    // --------------------------------------------------------- K/V staging
-    u32x4 kreg[KPT];
-    u32x4 vreg[VPT][2];
-    auto fetch = [&](int j) {
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            const int c = tid + u * NT;
-            if (KCH % NT == 0 || c < KCH) {
-                const int row = c / (D / 8), c8 = c % (D / 8);
-                kreg[u] = *(const u32x4 *)(kg + (size_t)(j * BLK + row) * D + c8 * 8);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            const int t = tid + u * NT;
-            if (VTASK % NT == 0 || t < VTASK) {
-                const int kp = t % 16, c8 = t / 16;
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int krow = j * BLK + 2 * kp + e;
-                    u32x4 x = *(const u32x4 *)(vg + (size_t)krow * D + c8 * 8);
-                    // padded keys: zero V so that p = 0 never meets a NaN
-                    vreg[u][e] = krow < len ? x : u32x4{0, 0, 0, 0};
-                }
-            }
-        }
-    };
-    auto deposit = [&](int buf) {
-        uint16_t *kl = lds + buf * BUF;
-        uint16_t *vt = kl + KSZ;
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            const int c = tid + u * NT;
-            if (KCH % NT == 0 || c < KCH) {
-                const int row = c / (D / 8), c8 = c % (D / 8);
-                *(u32x4 *)(kl + row * KROW + c8 * 8) = kreg[u];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            const int t = tid + u * NT;
-            if (VTASK % NT == 0 || t < VTASK) {
-                const int kp = t % 16, c8 = t / 16;
-                const int pos = vt_pos(2 * kp);
-                const u32x4 a = vreg[u][0], bb = vreg[u][1];
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t even = (a[w] & 0xFFFFu) | (bb[w] << 16);
-                    const uint32_t odd = (a[w] >> 16) | (bb[w] & 0xFFFF0000u);
-                    const int row = c8 * 8 + 2 * w;
-                    *(uint32_t *)(vt + vt_off(row, pos)) = even;
-                    *(uint32_t *)(vt + vt_off(row + 1, pos)) = odd;
-                }
-            }
-        }
-    };
-
-    fetch(jlo);
-    deposit(0);
-    __syncthreads();
-
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    // transposing-read coordinates of this lane inside its 16-lane group
+    const int grp16 = lane >> 4, li = lane & 15;
+    const int tr_row = 4 * half + (li >> 2);            // + 16 s (+ 8)
+    const int tr_col = 16 * (grp16 & 1) + 4 * (li & 3); // + 32 m
 
     for (int j = jlo; j <= jhi; ++j) {
-        const int cur = (j - jlo) & 1;
-        const bool more = j < jhi;
-        if (more)
-            fetch(j + 1);
+        const int stage = (j - jlo) % NSTAGE;
+        // this wave's loads for block j are done once at most the loads of the
+        // younger blocks remain; then the barrier makes every wave's share visible
+        // and frees the buffer read in the previous step
+        if (!TRACE && j + NSTAGE - 2 <= jhi)
+            wait_vm_lgkm0<(NSTAGE - 2) * LPT>();
+        else
+            wait_vm_lgkm0<0>();
+        workgroup_barrier();
+        if (j + NSTAGE - 1 <= jhi)
+            issue(j + NSTAGE - 1, (j - jlo + NSTAGE - 1) % NSTAGE);
+        const bool pad_block = j == nb - 1 && (len & (BLK - 1)) != 0;
+        if (pad_block) {
+            // the sequence ends inside this block: zero its V rows past the end
+            // (whole rows, so the chunk swizzle does not matter), so that p = 0
+            // never multiplies NaN or Inf padding; the last block is never
+            // reloaded into this buffer
+            uint8_t *vz = lds + stage * STAGE + T::BYTES;
+            const int r0 = len - j * BLK;
+            for (int x = tid; x < (BLK - r0) * T::CPR; x += NT)
+                *(u32x4 *)(vz + (r0 * T::CPR + x) * 16) = u32x4{0, 0, 0, 0};
+            wait_vm_lgkm0<63>();
+            workgroup_barrier();
+        }
 
         if (j >= lo_w && j <= hi_w) {
-            const uint16_t *kl = lds + cur * BUF;
-            const uint16_t *vt = kl + KSZ;
+            const uint8_t *kl = lds + stage * STAGE;
+            const uint8_t *vl = kl + T::BYTES;
 
             // S^T = K_j Q_i^T  (rows: keys, columns: queries)
             f32x16 s;
@@ -267,12 +300,13 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
                 s[r] = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 a = as_bf16x8(*(const u32x4 *)(kl + col * KROW + ks * 16 + half * 8));
+                const int c = (2 * ks + half) ^ T::k_swz(col);
+                const bf16x8 a = as_bf16x8(*(const u32x4 *)(kl + col * D * 2 + c * 16));
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
             }
 
             // padding and causal masks: only the last real block and the diagonal
-            const bool need_mask = (j == nb - 1 && (len & (BLK - 1)) != 0) || (CAUSAL && j == i);
+            const bool need_mask = pad_block || (CAUSAL && j == i);
             uint32_t part = 0;
             if (need_mask) {
 #pragma unroll
@@ -324,23 +358,25 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
                 lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
                 pk[u] = __builtin_bit_cast(uint32_t, pr);
             }
-            const bf16x8 pb0 = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
-            const bf16x8 pb1 = as_bf16x8(u32x4{pk[4], pk[5], pk[6], pk[7]});
+            const bf16x8 pb[2] = {as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]}),
+                                  as_bf16x8(u32x4{pk[4], pk[5], pk[6], pk[7]})};
 
-            // O^T += V_j^T P^T
+            // O^T += V_j^T P^T; the V^T operand comes from transposing reads
+            const uint32_t vrow = (uint32_t)(size_t)(lds_u8 *)(vl + tr_row * D * 2 + (tr_col & 7) * 2);
+            const int swz = T::v_swz(tr_row); // equal for rows +8, +16, +24
 #pragma unroll
             for (int m = 0; m < NMT; ++m) {
-                const int row = m * 32 + col;
-                const bf16x8 a0 = as_bf16x8(*(const u32x4 *)(vt + vt_off(row, half * 8)));
-                const bf16x8 a1 = as_bf16x8(*(const u32x4 *)(vt + vt_off(row, 16 + half * 8)));
-                oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, pb0, oacc[m], 0, 0, 0);
-                oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, pb1, oacc[m], 0, 0, 0);
+                const int cp = (4 * m + (tr_col >> 3)) ^ swz;
+                u32x2 r0, r1, r2, r3;
+                tr_tile<D * 2>(vrow + cp * 16, r0, r1, r2, r3);
+                const bf16x4 q0 = __builtin_bit_cast(bf16x4, r0), q1 = __builtin_bit_cast(bf16x4, r1);
+                const bf16x4 q2 = __builtin_bit_cast(bf16x4, r2), q3 = __builtin_bit_cast(bf16x4, r3);
+                const bf16x8 a0 = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+                const bf16x8 a1 = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, pb[0], oacc[m], 0, 0, 0);
+                oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, pb[1], oacc[m], 0, 0, 0);
             }
         }
-
-        if (more)
-            deposit(cur ^ 1);
-        __syncthreads();
     }
 
     // ------------------------------------------------------------- finalize
@@ -377,21 +413,23 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
     }
 }
 
-template <int D, int MQ, bool CAUSAL, bool TRACE>
+template <int D, int MQ, int NSTAGE, bool CAUSAL, bool TRACE>
 hipError_t launch_t(const Launch &a, const Params &p)
 {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, MQ, CAUSAL, TRACE>), dim3(p.total), dim3(MQ * 64), 0,
-                       a.stream, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MQ, NSTAGE, CAUSAL, TRACE>), dim3(p.total),
+                       dim3(MQ * 64), 0, a.stream, p);
     return hipGetLastError();
 }
 
-template <int D, int MQ>
+template <int D, int MQ, int NSTAGE>
 hipError_t launch_d(const Launch &a, const Params &p)
 {
     const bool tr = a.active != nullptr;
     if (a.causal)
-        return tr ? launch_t<D, MQ, true, true>(a, p) : launch_t<D, MQ, true, false>(a, p);
-    return tr ? launch_t<D, MQ, false, true>(a, p) : launch_t<D, MQ, false, false>(a, p);
+        return tr ? launch_t<D, MQ, NSTAGE, true, true>(a, p)
+                  : launch_t<D, MQ, NSTAGE, true, false>(a, p);
+    return tr ? launch_t<D, MQ, NSTAGE, false, true>(a, p)
+              : launch_t<D, MQ, NSTAGE, false, false>(a, p);
 }
 
 } // namespace
@@ -416,9 +454,9 @@ hipError_t launch_fwd_bf16(const Launch &a)
     p.total = a.batch * a.heads * p.ngroups;
     p.c = a.scale * LOG2E;
     switch (a.head_dim) {
-    case 32: return launch_d<32, MQ>(a, p);
-    case 64: return launch_d<64, MQ>(a, p);
-    case 128: return launch_d<128, MQ>(a, p);
+    case 32: return launch_d<32, MQ, 4>(a, p);
+    case 64: return launch_d<64, MQ, 4>(a, p);
+    case 128: return launch_d<128, MQ, 4>(a, p);
     default: return hipErrorInvalidValue;
     }
 }
