@@ -109,7 +109,7 @@ def time_workload(key, steps, warmup, cold=False, log=print):
     return dict(key=key, w=w, d=d, acc=acc, wall=wall, per_launch=per_launch, steps=steps)
 
 
-def cpu_baseline(r, target_flops=1.5e11, log=print):
+def cpu_baseline(r, target_flops=1.0e12, log=print):
     """Time the fp64 oracle on a bounded, evenly spread sample of query blocks
     (every head) of the same workload, on this host's cores."""
     import oracle

@@ -52,6 +52,13 @@ def load(path=LIB_PATH):
     if not os.path.exists(path):
         raise BslError(BSL_E_UNSUPPORTED,
                        f"{path} is not built; run `python -m block_sparse_local_amd.build`")
+    # torch's wheel carries its own HIP runtime, which it asks for by file name;
+    # loading torch first lets libbsl's libamdhip64.so.7 dependency resolve to
+    # that same copy, so the process has one HIP runtime, not two.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i32 = ctypes.c_void_p, ctypes.c_int32
     lib.bsl_create.argtypes = [ctypes.POINTER(BslDesc), ctypes.POINTER(vp)]

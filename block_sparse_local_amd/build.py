@@ -43,7 +43,7 @@ def build(out=LIB, extra=(), verbose=False):
     with tempfile.TemporaryDirectory(prefix="bsl_build_") as tmp:
         objs = []
         for s in SOURCES:
-            obj = os.path.join(tmp, s + ".o")
+            obj = os.path.join(tmp, os.path.basename(s) + ".o")
             _compile(os.path.join(CSRC, s), obj, extra)
             objs.append(obj)
         link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out + ".tmp"]

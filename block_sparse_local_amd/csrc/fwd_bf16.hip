@@ -146,8 +146,9 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
     constexpr int NKS = D / 16;                 // 16-deep steps of the score contraction
     constexpr int STAGE = 2 * T::BYTES;         // K tile then V tile
     constexpr int SLOTS = STAGE / 16;           // 16-byte slots per stage
-    static_assert(SLOTS % NT == 0, "each thread issues the same number of loads");
-    constexpr int LPT = SLOTS / NT;             // direct-to-LDS loads per thread per block
+    static_assert(SLOTS % NT == 0 || NT % SLOTS == 0, "slots split evenly over waves");
+    // direct-to-LDS loads per thread per block (waves past the last slot issue none)
+    constexpr int LPT = SLOTS >= NT ? SLOTS / NT : 1;
     static_assert(T::BYTES % (64 * 16) == 0, "a wave's load covers only K or only V");
     static_assert(D % 32 == 0 && D <= 128, "head_dim must be 32, 64 or 128");
     static_assert(NSTAGE >= 2, "ring depth");
@@ -210,6 +211,18 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
     int jhi = i0 + MQ - 1 + R > nb - 1 ? nb - 1 : i0 + MQ - 1 + R;
     if (CAUSAL && jhi > i0 + MQ - 1)
         jhi = i0 + MQ - 1;
+    // Sweep order.  A full-width group visits key block j at step j mod P (P =
+    // the width of a full group's band union), so the neighbouring groups that
+    // share a halo block (on the same XCD, run at the same time) ask for it in
+    // the same step and L2 serves all but the first request.  Softmax
+    // accumulation does not depend on the order of the blocks.
+    const int L = jhi - jlo + 1;
+    const int P = CAUSAL ? MQ + R : MQ + 2 * R;
+    const int rot = L == P ? (P - jlo % P) % P : 0;
+    auto block_at = [&](int t) {
+        const int x = t + rot;
+        return jlo + (x >= L ? x - L : x);
+    };
 
     // ------------------------------------------- K/V ring: direct-to-LDS
     // Slot s of a stage (16 bytes at stage + 16 s) holds K (s < SLOTS/2) or V;
@@ -220,6 +233,8 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
 #pragma unroll
         for (int u = 0; u < LPT; ++u) {
             const int s = u * NT + tid;
+            if (SLOTS < NT && s >= SLOTS)
+                continue; // whole waves only: SLOTS is a multiple of 64
             const bool is_v = s >= SLOTS / 2;
             const int t = is_v ? s - SLOTS / 2 : s;
             const int r = t / T::CPR, cp = t % T::CPR;
@@ -245,8 +260,8 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
     // start the ring before waiting on anything
 #pragma unroll
     for (int a = 0; a < NSTAGE - 1; ++a)
-        if (jlo + a <= jhi)
-            issue(jlo + a, a);
+        if (a < L)
+            issue(block_at(a), a);
 
     f32x16 oacc[NMT];
 #pragma unroll
@@ -263,24 +278,25 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
     const int tr_row = 4 * half + (li >> 2);            // + 16 s (+ 8)
     const int tr_col = 16 * (grp16 & 1) + 4 * (li & 3); // + 32 m
 
-    for (int j = jlo; j <= jhi; ++j) {
-        const int stage = (j - jlo) % NSTAGE;
-        // this wave's loads for block j are done once at most the loads of the
-        // younger blocks remain; then the barrier makes every wave's share visible
+    for (int t = 0; t < L; ++t) {
+        const int j = block_at(t);
+        const int stage = t % NSTAGE;
+        // this wave's loads for step t are done once at most the loads of the
+        // younger steps remain; then the barrier makes every wave's share visible
         // and frees the buffer read in the previous step
-        if (!TRACE && j + NSTAGE - 2 <= jhi)
+        if (!TRACE && t + NSTAGE - 2 < L)
             wait_vm_lgkm0<(NSTAGE - 2) * LPT>();
         else
             wait_vm_lgkm0<0>();
         workgroup_barrier();
-        if (j + NSTAGE - 1 <= jhi)
-            issue(j + NSTAGE - 1, (j - jlo + NSTAGE - 1) % NSTAGE);
+        if (t + NSTAGE - 1 < L)
+            issue(block_at(t + NSTAGE - 1), (t + NSTAGE - 1) % NSTAGE);
         const bool pad_block = j == nb - 1 && (len & (BLK - 1)) != 0;
         if (pad_block) {
             // the sequence ends inside this block: zero its V rows past the end
             // (whole rows, so the chunk swizzle does not matter), so that p = 0
-            // never multiplies NaN or Inf padding; the last block is never
-            // reloaded into this buffer
+            // never multiplies NaN or Inf padding; a later block loaded into
+            // this buffer overwrites every row
             uint8_t *vz = lds + stage * STAGE + T::BYTES;
             const int r0 = len - j * BLK;
             for (int x = tid; x < (BLK - r0) * T::CPR; x += NT)
@@ -434,9 +450,22 @@ hipError_t launch_d(const Launch &a, const Params &p)
 
 } // namespace
 
+// Query blocks (= waves) per workgroup and K/V ring depth: compile-time tuning
+// knobs.  Measured on c4 (d 128, R 8) and c5 (d 64, R 2): 4 and 3 are best;
+// 8 query blocks per workgroup, two query blocks per wave, deeper rings and a
+// software-pipelined step (scores of block j+1 issued before the softmax of
+// block j) were all slower, each by losing occupancy.
+#ifndef BSL_BF16_MQ
+#define BSL_BF16_MQ 4
+#endif
+#ifndef BSL_BF16_NSTAGE
+#define BSL_BF16_NSTAGE 3
+#endif
+
 hipError_t launch_fwd_bf16(const Launch &a)
 {
-    constexpr int MQ = 4;
+    constexpr int MQ = BSL_BF16_MQ;
+    constexpr int NS = BSL_BF16_NSTAGE;
     Params p;
     p.q = (const uint16_t *)a.q;
     p.k = (const uint16_t *)a.k;
@@ -454,9 +483,9 @@ hipError_t launch_fwd_bf16(const Launch &a)
     p.total = a.batch * a.heads * p.ngroups;
     p.c = a.scale * LOG2E;
     switch (a.head_dim) {
-    case 32: return launch_d<32, MQ, 4>(a, p);
-    case 64: return launch_d<64, MQ, 4>(a, p);
-    case 128: return launch_d<128, MQ, 4>(a, p);
+    case 32: return launch_d<32, MQ, NS>(a, p);
+    case 64: return launch_d<64, MQ, NS>(a, p);
+    case 128: return launch_d<128, MQ, NS>(a, p);
     default: return hipErrorInvalidValue;
     }
 }
