@@ -172,7 +172,7 @@ def summarize(r, traffic=None):
         roof = {"bound": "hbm", "achieved": alg_bytes / mean_launch / 1e9, "peak": 8000.0,
                 "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": flops / mean_launch / 1e12,
+        roof = {"bound": bound, "achieved": flops / mean_launch / 1e12,
                 "peak": acc["flops_peak"] / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic

@@ -58,6 +58,8 @@ def account(lens, heads, d, radius, causal, dtype="bf16"):
     peak = MI355X_BF16_DENSE_FLOPS if dtype == "bf16" else MI355X_FP32_VECTOR_FLOPS
     t_mfma = flops / peak
     t_hbm = nbytes / MI355X_HBM_BYTES
+    # the bf16 path computes on MFMA; the fp32 path on the vector ALUs
+    compute_unit = "mfma" if dtype == "bf16" else "alu"
     return dict(useful_pairs=up, block_pairs=bp, tokens=tokens, useful_flops=flops,
                 computed_flops=computed, alg_bytes=nbytes, t_mfma=t_mfma, t_hbm=t_hbm,
-                bound="hbm" if t_hbm >= t_mfma else "mfma", flops_peak=peak)
+                bound="hbm" if t_hbm >= t_mfma else compute_unit, flops_peak=peak)
