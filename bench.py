@@ -39,22 +39,64 @@ if ROOT not in sys.path:
 KERNEL_SOURCES = ["block_sparse_local_amd/csrc/fwd_bf16.hip", "block_sparse_local_amd/csrc/launch.h"]
 
 
+def _scan(src, on_comment, on_space):
+    """Walk C/C++ source; string and character literals are copied verbatim,
+    comments and whitespace runs are replaced by what the callbacks return."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i) and on_comment:
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i) and on_comment:
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif c.isspace() and on_space:
+            j = i
+            while j < n and src[j].isspace():
+                j += 1
+            out.append(on_space(src[i:j]))
+            i = j
+        else:
+            out.append(c)
+            i += 1
+    return "".join(out)
+
+
+def code_text(src):
+    """C/C++ source with comments removed and every whitespace run outside
+    string and character literals reduced to one newline (if it held one, for
+    the preprocessor) or one space: two sources with the same code_text compile
+    to the same kernel, so a comment edit does not void the stored counter
+    summaries."""
+    bare = _scan(src, True, None)
+    return _scan(bare, False, lambda ws: "\n" if "\n" in ws else " ").strip()
+
+
 def kernel_sha():
+    """Hash of the bf16 kernel's code (comments and layout excluded)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode("utf-8"))
     return h.hexdigest()[:16]
 
 
 def stored_traffic(workload_key):
     """Bytes per launch from the committed counter summary, if it was taken on
-    the current kernel source."""
+    the current kernel code."""
     path = os.path.join(ROOT, "profiles", f"pmc_traffic_fwd_bf16_{workload_key}.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    sha = re.search(r"^kernel_source_sha256_16:\s*(\w+)", text, re.M)
+    sha = re.search(r"^kernel_code_sha256_16:\s*(\w+)", text, re.M)
     val = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
     if not sha or not val or sha.group(1) != kernel_sha():
         return None

@@ -22,8 +22,9 @@
 //    MFMA operand reads below hit distinct LDS banks.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    in the 32x32 accumulator each lane then owns one query (column) and 16 of
-//    the 32 keys, so the row maximum is 15 in-register max ops plus one exchange
-//    with the lane 32 away, and m, l and the rescale factor stay per lane.
+//    the 32 keys, so the row maximum is 15 in-register max ops, plus one
+//    exchange with the lane 32 away on the rare steps that move the reference
+//    maximum; m, l and the rescale factor stay per lane.
 //  * The output is also formed transposed, O^T += V^T P^T.  P^T is the MFMA B
 //    operand straight from the score accumulator (rounded to bf16), with the key
 //    order inside each 16-key step permuted to the accumulator's register order;
@@ -345,14 +346,18 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
                     p.active[slot] = j;
             }
 
-            // running maximum (log2 units), moved only when it grows a lot
+            // running maximum (log2 units), moved only when it grows a lot.  A
+            // query's 32 scores sit in two lanes (l, l+32), 16 each; the column
+            // maximum exceeds the bound exactly when one half's maximum does, so
+            // the lanes test their own half and exchange only on the rare move
+            // (the scale is positive, so scaling commutes with the maximum).
             float mx = s[0];
 #pragma unroll
             for (int r = 1; r < 16; ++r)
                 mx = fmaxf(mx, s[r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mt = mx * p.c;
-            if (__ballot(mt > m_used + RESCALE_SLACK) != 0) {
+            const float mt_half = mx * p.c;
+            if (__ballot(mt_half > m_used + RESCALE_SLACK) != 0) {
+                const float mt = fmaxf(mt_half, __shfl_xor(mt_half, 32));
                 const float mn = fmaxf(m_used, mt);
                 const float alpha = __builtin_amdgcn_exp2f(m_used - mn);
 #pragma unroll
@@ -451,10 +456,15 @@ hipError_t launch_d(const Launch &a, const Params &p)
 } // namespace
 
 // Query blocks (= waves) per workgroup and K/V ring depth: compile-time tuning
-// knobs.  Measured on c4 (d 128, R 8) and c5 (d 64, R 2): 4 and 3 are best;
-// 8 query blocks per workgroup, two query blocks per wave, deeper rings and a
-// software-pipelined step (scores of block j+1 issued before the softmax of
-// block j) were all slower, each by losing occupancy.
+// knobs.  Measured on the d 128 / R 8 and d 64 / R 2 workloads: 4 and 3 are
+// best.  Slower or no faster: 5, 6 or 8 query blocks per workgroup; rings of 2,
+// 4 or 5 stages; a software-pipelined step (scores of block j+1 issued before
+// the softmax of block j: 2 waves per SIMD instead of 3); all K operand reads
+// issued ahead; the transposing V reads grouped 8 per wait; wave priority
+// raised around the MFMA bursts; one wave per step issuing the whole ring
+// refill; 5 waves per SIMD at d 64; and a persistent kernel with two query
+// blocks per wave (1 wave per SIMD, whose MFMA, softmax and LDS waits then run
+// back to back).
 #ifndef BSL_BF16_MQ
 #define BSL_BF16_MQ 4
 #endif
