@@ -92,6 +92,8 @@ def kernel_sha():
 def stored_traffic(workload_key):
     """Bytes per launch from the committed counter summary, if it was taken on
     the current kernel code."""
+    if os.environ.get("BSL_LIBRARY"):
+        return None  # the stored counters describe the in-tree build only
     path = os.path.join(ROOT, "profiles", f"pmc_traffic_fwd_bf16_{workload_key}.txt")
     if not os.path.exists(path):
         return None
@@ -224,6 +226,7 @@ def summarize(r, traffic=None):
         "mean_launch_us": mean_launch * 1e6,
         "median_launch_us": float(np.median(r["per_launch"])) * 1e6,
         "min_launch_us": float(r["per_launch"].min()) * 1e6,
+        "p90_launch_us": float(np.percentile(r["per_launch"], 90)) * 1e6,
         "alg_bytes": alg_bytes,
         "useful_flops": flops,
         "computed_flops": acc["computed_flops"],
@@ -305,6 +308,8 @@ def main():
     }
     if args.cold:
         line["timing"] = "cold: 1 GiB overwritten between steps"
+    if os.environ.get("BSL_LIBRARY"):
+        line["library"] = os.environ["BSL_LIBRARY"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(r, log=log)
     del r

@@ -15,7 +15,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libbsl.so")
+# BSL_LIBRARY selects another build of the same library (a design variant made
+# by `build.py --variant ... --out ...`); unset, the in-tree build is used
+LIB_PATH = os.environ.get("BSL_LIBRARY") or os.path.join(HERE, "libbsl.so")
 
 BSL_OK, BSL_E_INVALID, BSL_E_UNSUPPORTED, BSL_E_DEVICE, BSL_E_NOMEM = range(5)
 BSL_BF16, BSL_F32 = 0, 1

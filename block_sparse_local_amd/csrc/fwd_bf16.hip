@@ -56,10 +56,38 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
+// Design switches.  Each names one design choice of this kernel; the default
+// is the shipped kernel, and every alternative computes the same result (same
+// work, same masks, same arithmetic up to rounding), so that a build with one
+// choice reverted can be timed and counted against the shipped one:
+//   BSL_SWIZZLE       1: XOR-swizzle 16-byte chunks in LDS; 0: row-major tiles
+//   BSL_XCD_REMAP     1: give each XCD a contiguous run of query groups;
+//                     0: hardware order (groups dealt round robin to XCDs)
+//   BSL_ROTATE        1: a full group visits key block j at step j mod P;
+//                     0: every group sweeps its band from the left
+//   BSL_RESCALE_SLACK move the reference maximum only when a row's maximum
+//                     exceeds it by more than this (log2 units; 0: on any rise)
+//   BSL_LAZY_EXCHANGE 1: exchange half-column maxima only on a move; 0: always
+#ifndef BSL_SWIZZLE
+#define BSL_SWIZZLE 1
+#endif
+#ifndef BSL_XCD_REMAP
+#define BSL_XCD_REMAP 1
+#endif
+#ifndef BSL_ROTATE
+#define BSL_ROTATE 1
+#endif
+#ifndef BSL_RESCALE_SLACK
+#define BSL_RESCALE_SLACK 8.0f
+#endif
+#ifndef BSL_LAZY_EXCHANGE
+#define BSL_LAZY_EXCHANGE 1
+#endif
+
 constexpr int BLK = 32;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
-constexpr float RESCALE_SLACK = 8.0f; // in log2 units
+constexpr float RESCALE_SLACK = BSL_RESCALE_SLACK; // in log2 units
 
 struct Params {
     const uint16_t *q, *k, *v;
@@ -77,6 +105,8 @@ struct Params {
 // neighbouring query groups.  A bijection on [0, total).
 __device__ __forceinline__ int xcd_remap(int g, int total)
 {
+    if (!BSL_XCD_REMAP)
+        return g;
     const int per = total / 8, extra = total % 8;
     const int x = g % 8, k = g / 8;
     return (x < extra ? x * (per + 1) : extra * (per + 1) + (x - extra) * per) + k;
@@ -95,12 +125,12 @@ struct Tile {
     static constexpr int ROWS_PER_256B = 16 / CPR;
     // K is read as 32 rows x one logical chunk: spread 16 consecutive rows over
     // 16 distinct chunk positions of a 256-byte bank window.
-    __device__ static __forceinline__ int k_swz(int r) { return (r / ROWS_PER_256B) % CPR; }
+    __device__ static __forceinline__ int k_swz(int r) { return BSL_SWIZZLE ? (r / ROWS_PER_256B) % CPR : 0; }
     // V is read 4 consecutive rows x 4 consecutive logical chunks at a time
     // (transposing reads): put the 4 rows in 4 different aligned 4-chunk sets.
     __device__ static __forceinline__ int v_swz(int r)
     {
-        return ((r / ROWS_PER_256B) & (CPR / 4 - 1)) << 2;
+        return BSL_SWIZZLE ? ((r / ROWS_PER_256B) & (CPR / 4 - 1)) << 2 : 0;
     }
 };
 
@@ -219,7 +249,7 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
     // accumulation does not depend on the order of the blocks.
     const int L = jhi - jlo + 1;
     const int P = CAUSAL ? MQ + R : MQ + 2 * R;
-    const int rot = L == P ? (P - jlo % P) % P : 0;
+    const int rot = BSL_ROTATE && L == P ? (P - jlo % P) % P : 0;
     auto block_at = [&](int t) {
         const int x = t + rot;
         return jlo + (x >= L ? x - L : x);
@@ -355,9 +385,9 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
 #pragma unroll
             for (int r = 1; r < 16; ++r)
                 mx = fmaxf(mx, s[r]);
-            const float mt_half = mx * p.c;
+            const float mt_half = BSL_LAZY_EXCHANGE ? mx * p.c : fmaxf(mx, __shfl_xor(mx, 32)) * p.c;
             if (__ballot(mt_half > m_used + RESCALE_SLACK) != 0) {
-                const float mt = fmaxf(mt_half, __shfl_xor(mt_half, 32));
+                const float mt = BSL_LAZY_EXCHANGE ? fmaxf(mt_half, __shfl_xor(mt_half, 32)) : mt_half;
                 const float mn = fmaxf(m_used, mt);
                 const float alpha = __builtin_amdgcn_exp2f(m_used - mn);
 #pragma unroll

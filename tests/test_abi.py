@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -87,3 +88,21 @@ def test_binding_raises_on_error(lib):
     with pytest.raises(bsl.BslError) as e:
         bsl.bsl_create(bsl.BslDesc(head_dim=48))
     assert e.value.status == bsl.BSL_E_UNSUPPORTED
+
+
+def test_library_override_is_loud_when_missing(tmp_path):
+    """BSL_LIBRARY points the binding at another build; a missing one is an error,
+    never a silent fall back to anything else."""
+    missing = tmp_path / "not_built.so"
+    code = ("import sys\n"
+            "from block_sparse_local_amd import bsl\n"
+            "try:\n"
+            "    bsl.load()\n"
+            "except bsl.BslError as e:\n"
+            "    print('BslError', e)\n"
+            "    sys.exit(3)\n")
+    env = dict(os.environ, BSL_LIBRARY=str(missing))
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 3, r.stdout + r.stderr
+    assert str(missing) in r.stdout

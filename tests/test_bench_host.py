@@ -65,6 +65,10 @@ def test_stored_traffic_needs_the_current_kernel_code(tmp_path, monkeypatch):
     assert bench.stored_traffic("cx") == 1.5e9
     (csrc / "k.hip").write_text(SRC.replace("x + 1", "x - 1"))
     assert bench.stored_traffic("cx") is None
+    # another build of the library (a design variant) never borrows the summary
+    (csrc / "k.hip").write_text(SRC)
+    monkeypatch.setenv("BSL_LIBRARY", str(tmp_path / "variant.so"))
+    assert bench.stored_traffic("cx") is None
 
 
 def test_more_than_one_gpu_is_refused():
@@ -120,3 +124,5 @@ def test_summarize_roofline_fields():
     assert t_step == pytest.approx(1.05e-3)
     assert extra["useful_tflops"] == pytest.approx(acc["useful_flops"] / 1.05e-3 / 1e12)
     assert extra["tokens_per_s"] == pytest.approx(acc["tokens"] / 1.05e-3)
+    assert extra["median_launch_us"] == pytest.approx(1.0e3)
+    assert extra["p90_launch_us"] == pytest.approx(1.0e3)
