@@ -10,7 +10,8 @@ shape [batch, heads, n, d] holding the exact (bf16- or fp32-rounded) values a
 GPU consumes; results are float64.  The computation follows the NucleoByte
 project page, section 3 ("Localized Block-Sparse Attention Matrix" for the
 band rule, "Softmax Normalization & Online Numerical Stability" for the scores
-and the softmax); see orc.c for the definitions.
+and the softmax, "Custom Backpropagation" for the gradients); see orc.c for
+the definitions.
 
 Parity pins (what ties each routine to something other than itself) live in
 ``tests/test_oracle_*.py``.  No oracle routine is "parity unpinned".
@@ -47,8 +48,13 @@ def _declare(lib):
                                            _f64p, i]
     lib.orc_forward_recurrence_f64.argtypes = [i, i, i, i, i, i, i, ctypes.c_double, _i32p,
                                                _f32p, _f32p, _f32p, _f64p]
+    lib.orc_backward_f64.argtypes = [i, i, i, i, i, i, i, ctypes.c_double, _i32p, _f32p, _f32p,
+                                     _f32p, _f32p, _f64p, _f64p, _f64p, i]
+    lib.orc_backward_blocks_f64.argtypes = [i, i, i, i, i, i, i, ctypes.c_double, _i32p, _f32p,
+                                            _f32p, _f32p, _f32p, ctypes.c_int64, _i32p, _f64p,
+                                            _f64p, _f64p, i]
     for name in ("orc_active_blocks", "orc_masks", "orc_forward_f64", "orc_forward_blocks_f64",
-                 "orc_forward_recurrence_f64"):
+                 "orc_forward_recurrence_f64", "orc_backward_f64", "orc_backward_blocks_f64"):
         getattr(lib, name).restype = i
     return lib
 
@@ -179,3 +185,46 @@ def forward_recurrence(q, k, v, seqlens=None, bsize=32, radius=1, causal=False, 
                                           _ptr(k, _f32p), _ptr(v, _f32p), _ptr(o, _f64p)),
            "orc_forward_recurrence_f64")
     return o
+
+
+def backward(q, k, v, dout, seqlens=None, bsize=32, radius=1, causal=False, scale=0.0,
+             nthreads=None, lib=None):
+    """Gradients of the forward with respect to q, k, v for the output gradient
+    ``dout`` (float32 [b,h,n,d]).  Returns (dq, dk, dv), float64 [b,h,n,d]."""
+    lib = lib or load()
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    batch, heads, n, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, k, v, dout shapes differ")
+    s = _lens(batch, n, seqlens)
+    dq = np.empty((batch, heads, n, d), dtype=np.float64)
+    dk = np.empty_like(dq)
+    dv = np.empty_like(dq)
+    _check(lib.orc_backward_f64(batch, heads, n, d, bsize, radius, int(causal), float(scale),
+                                _ptr(s, _i32p), _ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p),
+                                _ptr(dout, _f32p), _ptr(dq, _f64p), _ptr(dk, _f64p),
+                                _ptr(dv, _f64p), nthreads or default_threads()),
+           "orc_backward_f64")
+    return dq, dk, dv
+
+
+def backward_blocks(q, k, v, dout, sel, seqlens=None, bsize=32, radius=1, causal=False,
+                    scale=0.0, nthreads=None, lib=None):
+    """For each (b, h, i) in ``sel``: dq of query block i and dk, dv of key
+    block i.  Returns (dq, dk, dv), each float64 [m, bsize, d]."""
+    lib = lib or load()
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    batch, heads, n, d = q.shape
+    s = _lens(batch, n, seqlens)
+    sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 3)
+    m = sel.shape[0]
+    dq = np.empty((m, bsize, d), dtype=np.float64)
+    dk = np.empty_like(dq)
+    dv = np.empty_like(dq)
+    _check(lib.orc_backward_blocks_f64(batch, heads, n, d, bsize, radius, int(causal),
+                                       float(scale), _ptr(s, _i32p), _ptr(q, _f32p),
+                                       _ptr(k, _f32p), _ptr(v, _f32p), _ptr(dout, _f32p), m,
+                                       _ptr(sel, _i32p), _ptr(dq, _f64p), _ptr(dk, _f64p),
+                                       _ptr(dv, _f64p), nthreads or default_threads()),
+           "orc_backward_blocks_f64")
+    return dq, dk, dv

@@ -33,6 +33,15 @@
  * it is the only reading under which the probabilities sum to one).  The tests
  * compare the two routines; they are independent formulations of one result.
  *
+ * The backward routines (orc_backward_f64, orc_backward_blocks_f64) follow the
+ * same page's section 3, "Custom Backpropagation": a per-row correction
+ * D_t = sum_c dO_tc O_tc and dS_ts = P_ts (dO_t . V_s - D_t), with P the
+ * softmax above.  The page leaves the remaining gradients to the chain rule
+ * through S = scale Q K^T and O = P V, written out plainly:
+ *   dV_s = sum_t P_ts dO_t,  dQ_t = scale sum_s dS_ts K_s,  dK_s = scale sum_t dS_ts Q_t
+ * with t over valid rows and s over A(b,t); padded rows and keys get zero.
+ * O and P are recomputed here from Q, K, V in double (the exact forward).
+ *
  * Inputs are float (the exact bf16- or fp32-rounded values a GPU consumes);
  * every product and sum is taken in double.  Q, K, V, O are [batch][heads][n][d]
  * contiguous.  All routines return 0 on success and a negative code on bad
@@ -492,4 +501,235 @@ int orc_forward_recurrence_f64(int batch, int heads, int n, int d, int bsize, in
     free(sblk);
     free(acc);
     return 0;
+}
+
+/* ------------------------------------------------------------ backward pass */
+
+typedef struct {
+    problem fw;
+    const float *dout;
+} bproblem;
+
+/* Gradient contributions of query row t of (b, h), from the definition:
+ * recompute the row's kept keys, P and O, then D_t, dS_ts, and add
+ *   dq_row += scale * dS_ts K_s                      (always)
+ *   dk[s], dv[s] += scale * dS_ts Q_t, P_ts dO_t     (for keys s in [klo, khi))
+ * dk and dv point at key row klo.  Rows t >= len contribute nothing. */
+static void row_backward(const bproblem *bp, int b, int h, int t, double *sbuf, int32_t *sidx,
+                         double *orow, double *dq_row, int klo, int khi, double *dk, double *dv)
+{
+    const problem *p = &bp->fw;
+    const int len = seq_len(p->seqlens, b, p->n);
+    if (t >= len)
+        return;
+    const int64_t base = ((int64_t)b * p->heads + h) * p->n;
+    const int d = p->d;
+    /* P (in sbuf, over the kept keys sidx) and O of this row */
+    double lse;
+    row_definition(p, b, h, t, sbuf, sidx, orow, &lse, NULL);
+    int cnt = 0;
+    {
+        /* row_definition leaves exp(S - M) in sbuf for the kept keys in
+         * ascending order; recount them and normalise */
+        const int ib = t / p->bsize;
+        int s_lo = (ib - p->radius) * p->bsize, s_hi = (ib + p->radius + 1) * p->bsize;
+        if (s_lo < 0)
+            s_lo = 0;
+        if (s_hi > len)
+            s_hi = len;
+        for (int s = s_lo; s < s_hi; ++s)
+            if (pair_kept(t, s, len, p->bsize, p->radius, p->causal))
+                ++cnt;
+        double l = 0.0;
+        for (int e = 0; e < cnt; ++e)
+            l += sbuf[e];
+        for (int e = 0; e < cnt; ++e)
+            sbuf[e] /= l;
+    }
+    const float *q_row = p->q + (base + t) * d;
+    const float *dot_ = bp->dout + (base + t) * d;
+    double Dt = 0.0;
+    for (int c = 0; c < d; ++c)
+        Dt += (double)dot_[c] * orow[c];
+    for (int e = 0; e < cnt; ++e) {
+        const int s = sidx[e];
+        const double P = sbuf[e];
+        const float *vs = p->v + (base + s) * d;
+        double dP = 0.0;
+        for (int c = 0; c < d; ++c)
+            dP += (double)dot_[c] * (double)vs[c];
+        const double dS = P * (dP - Dt);
+        const float *ks = p->k + (base + s) * d;
+        if (dq_row)
+            for (int c = 0; c < d; ++c)
+                dq_row[c] += p->scale * dS * (double)ks[c];
+        if (s >= klo && s < khi) {
+            double *dks = dk + (int64_t)(s - klo) * d, *dvs = dv + (int64_t)(s - klo) * d;
+            for (int c = 0; c < d; ++c) {
+                dks[c] += p->scale * dS * (double)q_row[c];
+                dvs[c] += P * (double)dot_[c];
+            }
+        }
+    }
+}
+
+typedef struct {
+    const bproblem *bp;
+    int64_t nwork;
+    const int32_t *sel; /* NULL: every (b, h) slice; else (b, h, i) triples */
+    double *dq, *dk, *dv;
+    int64_t next;
+    pthread_mutex_t lock;
+    int failed;
+} bjob;
+
+static void *bworker(void *arg)
+{
+    bjob *jb = (bjob *)arg;
+    const problem *p = &jb->bp->fw;
+    const int maxkeys = (2 * p->radius + 1) * p->bsize;
+    const int d = p->d, B = p->bsize, nblk = p->n / B;
+    double *sbuf = (double *)malloc(sizeof(double) * (size_t)maxkeys);
+    int32_t *sidx = (int32_t *)malloc(sizeof(int32_t) * (size_t)maxkeys);
+    double *orow = (double *)malloc(sizeof(double) * (size_t)d);
+    if (!sbuf || !sidx || !orow) {
+        free(sbuf);
+        free(sidx);
+        free(orow);
+        pthread_mutex_lock(&jb->lock);
+        jb->failed = 1;
+        pthread_mutex_unlock(&jb->lock);
+        return NULL;
+    }
+    for (;;) {
+        pthread_mutex_lock(&jb->lock);
+        const int64_t w = jb->next++;
+        pthread_mutex_unlock(&jb->lock);
+        if (w >= jb->nwork)
+            break;
+        if (!jb->sel) {
+            /* whole slice (b, h): every row adds into its slice of dq, dk, dv */
+            const int b = (int)(w / p->heads), h = (int)(w % p->heads);
+            const int64_t off = ((int64_t)b * p->heads + h) * p->n * d;
+            for (int t = 0; t < p->n; ++t)
+                row_backward(jb->bp, b, h, t, sbuf, sidx, orow, jb->dq + off + (int64_t)t * d, 0,
+                             p->n, jb->dk + off, jb->dv + off);
+        } else {
+            /* one block index i: dQ of query block i, dK and dV of key block i;
+             * the latter gather every row whose band holds key block i */
+            const int b = jb->sel[3 * w], h = jb->sel[3 * w + 1], i = jb->sel[3 * w + 2];
+            double *dq = jb->dq + w * (int64_t)B * d;
+            double *dk = jb->dk + w * (int64_t)B * d, *dv = jb->dv + w * (int64_t)B * d;
+            for (int r = 0; r < B; ++r)
+                row_backward(jb->bp, b, h, i * B + r, sbuf, sidx, orow, dq + (int64_t)r * d, 0, 0,
+                             NULL, NULL);
+            for (int qi = i - p->radius; qi <= i + p->radius; ++qi) {
+                if (qi < 0 || qi >= nblk)
+                    continue;
+                for (int r = 0; r < B; ++r)
+                    row_backward(jb->bp, b, h, qi * B + r, sbuf, sidx, orow, NULL, i * B,
+                                 (i + 1) * B, dk, dv);
+            }
+        }
+    }
+    free(sbuf);
+    free(sidx);
+    free(orow);
+    return NULL;
+}
+
+static int run_bpool(bjob *jb, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 1024)
+        nthreads = 1024;
+    pthread_mutex_init(&jb->lock, NULL);
+    jb->next = 0;
+    jb->failed = 0;
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!tid)
+        return ORC_E_NOMEM;
+    int started = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        if (pthread_create(&tid[t], NULL, bworker, jb) != 0)
+            break;
+        ++started;
+    }
+    if (started == 0)
+        bworker(jb);
+    for (int t = 0; t < started; ++t)
+        pthread_join(tid[t], NULL);
+    free(tid);
+    pthread_mutex_destroy(&jb->lock);
+    return jb->failed ? ORC_E_NOMEM : 0;
+}
+
+/* Full backward: dq, dk, dv [batch][heads][n][d] (overwritten), from the
+ * forward's inputs and the output gradient dout [batch][heads][n][d]. */
+int orc_backward_f64(int batch, int heads, int n, int d, int bsize, int radius, int causal,
+                     double scale, const int32_t *seqlens, const float *q, const float *k,
+                     const float *v, const float *dout, double *dq, double *dk, double *dv,
+                     int nthreads)
+{
+    bproblem bp = {{batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v},
+                   dout};
+    int rc = check_problem(&bp.fw);
+    if (rc)
+        return rc;
+    const int64_t total = (int64_t)batch * heads * n * d;
+    if (total == 0)
+        return 0;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv)
+        return ORC_E_INVALID;
+    memset(dq, 0, sizeof(double) * (size_t)total);
+    memset(dk, 0, sizeof(double) * (size_t)total);
+    memset(dv, 0, sizeof(double) * (size_t)total);
+    bjob jb;
+    memset(&jb, 0, sizeof jb);
+    jb.bp = &bp;
+    jb.nwork = (int64_t)batch * heads;
+    jb.dq = dq;
+    jb.dk = dk;
+    jb.dv = dv;
+    return run_bpool(&jb, nthreads);
+}
+
+/* Selected block indices sel[w] = (b, h, i): dq [nsel][bsize][d] gets the rows
+ * of query block i, dk and dv [nsel][bsize][d] the rows of key block i. */
+int orc_backward_blocks_f64(int batch, int heads, int n, int d, int bsize, int radius, int causal,
+                            double scale, const int32_t *seqlens, const float *q, const float *k,
+                            const float *v, const float *dout, int64_t nsel, const int32_t *sel,
+                            double *dq, double *dk, double *dv, int nthreads)
+{
+    bproblem bp = {{batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v},
+                   dout};
+    int rc = check_problem(&bp.fw);
+    if (rc)
+        return rc;
+    if (nsel < 0)
+        return ORC_E_INVALID;
+    if (nsel == 0)
+        return 0;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || !sel)
+        return ORC_E_INVALID;
+    for (int64_t w = 0; w < nsel; ++w) {
+        const int32_t *s = sel + 3 * w;
+        if (s[0] < 0 || s[0] >= batch || s[1] < 0 || s[1] >= heads || s[2] < 0 ||
+            s[2] >= n / bsize)
+            return ORC_E_INVALID;
+    }
+    const size_t per = sizeof(double) * (size_t)nsel * (size_t)bsize * (size_t)d;
+    memset(dq, 0, per);
+    memset(dk, 0, per);
+    memset(dv, 0, per);
+    bjob jb;
+    memset(&jb, 0, sizeof jb);
+    jb.bp = &bp;
+    jb.nwork = nsel;
+    jb.sel = sel;
+    jb.dq = dq;
+    jb.dk = dk;
+    jb.dv = dv;
+    return run_bpool(&jb, nthreads);
 }

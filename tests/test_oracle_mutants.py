@@ -105,3 +105,95 @@ def test_mutant_is_caught(name):
         lib_path = obuild.build(out=os.path.join(tmp, "liborc_mutant.so"), src=path)
         lib = oracle.load(lib_path)
         assert _battery(lib) != [], f"mutant {name} slipped through every pin"
+
+
+# ------------------------------------------------------------ backward pass
+
+BWD_MUTANTS = {
+    "bwd_drop_D": ("const double dS = P * (dP - Dt);", "const double dS = P * dP;"),
+    "bwd_dq_no_scale": ("dq_row[c] += p->scale * dS * (double)ks[c];",
+                        "dq_row[c] += dS * (double)ks[c];"),
+    "bwd_dk_wrong_operand": ("dks[c] += p->scale * dS * (double)q_row[c];",
+                             "dks[c] += p->scale * dS * ((double)ks[c] + 0.0 * q_row[c]);"),
+    "bwd_dv_uses_dS": ("dvs[c] += P * (double)dot_[c];", "dvs[c] += dS * (double)dot_[c];"),
+    "bwd_unnormalised_P": ("            sbuf[e] /= l;\n", "            sbuf[e] /= 1.0;\n"),
+    "bwd_D_from_query": ("Dt += (double)dot_[c] * orow[c];",
+                         "Dt += (double)dot_[c] * (double)q_row[c];"),
+    "bwd_dP_from_keys": ("const float *vs = p->v + (base + s) * d;",
+                         "const float *vs = p->k + (base + s) * d;"),
+    "bwd_blocks_drop_last_row_block": ("qi <= i + p->radius; ++qi)", "qi < i + p->radius; ++qi)"),
+}
+
+
+def _fd_grad(lib, q, k, v, g, lens, bsize, radius, causal, which, idx):
+    def loss(x):
+        a = [q, k, v]
+        a[which] = x
+        o, _, _ = oracle.forward(*a, lens, bsize, radius, causal, nthreads=1, lib=lib)
+        return float(np.sum(o * g))
+    h = 2.0 ** -10
+    x = [q, k, v][which]
+
+    def central(hh):
+        up, dn = x.copy(), x.copy()
+        up[idx] += np.float32(hh)
+        dn[idx] -= np.float32(hh)
+        return (loss(up) - loss(dn)) / (2 * hh)
+    return (4 * central(h / 2) - central(h)) / 3
+
+
+def _bwd_battery(lib):
+    """Backward pins against a (possibly mutated) oracle; the forward used for
+    the finite differences is the unmodified one."""
+    failed = []
+    ref_lib = oracle.load()
+    rng = np.random.default_rng(99)
+    for bsize, nblk, radius, causal, lens in [(8, 5, 1, False, [40, 27]), (8, 5, 2, True, [40, 21])]:
+        n = nblk * bsize
+        lens = np.array(lens, dtype=np.int32)
+        q, k, v, g = [(np.round(rng.uniform(-1, 1, (2, 1, n, 8)) * 128) / 128).astype(np.float32)
+                      for _ in range(4)]
+        try:
+            dq, dk, dv = oracle.backward(q, k, v, g, lens, bsize, radius, causal, lib=lib)
+            for which, grad in enumerate((dq, dk, dv)):
+                for idx in [(0, 0, 5, 1), (0, 0, 33, 7), (1, 0, 20, 3)]:
+                    fd = _fd_grad(ref_lib, q, k, v, g, lens, bsize, radius, causal, which, idx)
+                    if not abs(fd - grad[idx]) <= 1e-8 + 1e-7 * abs(grad[idx]):
+                        failed.append("finite_differences")
+            for b in range(2):
+                if not np.allclose(dv[b].sum(axis=1), g[b, :, :lens[b]].sum(axis=1), atol=1e-12):
+                    failed.append("dv_sum")
+                if not np.max(np.abs(dk[b].sum(axis=1))) <= 1e-12:
+                    failed.append("dk_sum")
+            sel = np.array([[0, 0, i] for i in range(nblk)] + [[1, 0, i] for i in range(nblk)],
+                           dtype=np.int32)
+            bq, bk, bv = oracle.backward_blocks(q, k, v, g, sel, lens, bsize, radius, causal,
+                                                lib=lib)
+            for w, (b, h, i) in enumerate(sel):
+                rows = slice(i * bsize, (i + 1) * bsize)
+                if not (np.allclose(bq[w], dq[b, h, rows], atol=1e-13)
+                        and np.allclose(bk[w], dk[b, h, rows], atol=1e-13)
+                        and np.allclose(bv[w], dv[b, h, rows], atol=1e-13)):
+                    failed.append("blocks_vs_full")
+        except oracle.OracleError:
+            failed.append("error")
+    return sorted(set(failed))
+
+
+def test_unmodified_oracle_passes_backward_battery():
+    assert _bwd_battery(oracle.load()) == []
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(name):
+    old, new = BWD_MUTANTS[name]
+    with open(obuild.SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "orc_mutant.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        lib_path = obuild.build(out=os.path.join(tmp, "liborc_mutant.so"), src=path)
+        lib = oracle.load(lib_path)
+        assert _bwd_battery(lib) != [], f"mutant {name} slipped through every pin"
