@@ -23,7 +23,7 @@ BSL_OK, BSL_E_INVALID, BSL_E_UNSUPPORTED, BSL_E_DEVICE, BSL_E_NOMEM = range(5)
 BSL_BF16, BSL_F32 = 0, 1
 
 # every function include/bsl.h declares
-EXPORTS = ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_destroy",
+EXPORTS = ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_backward", "bsl_destroy",
            "bsl_status_string", "bsl_last_error", "bsl_version")
 
 
@@ -66,6 +66,7 @@ def load(path=LIB_PATH):
     lib.bsl_create.argtypes = [ctypes.POINTER(BslDesc), ctypes.POINTER(vp)]
     lib.bsl_forward.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.bsl_forward_traced.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.bsl_backward.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.bsl_destroy.argtypes = [vp]
     lib.bsl_status_string.argtypes = [ctypes.c_int]
     lib.bsl_status_string.restype = ctypes.c_char_p
@@ -73,7 +74,7 @@ def load(path=LIB_PATH):
     lib.bsl_last_error.restype = ctypes.c_char_p
     lib.bsl_version.argtypes = []
     lib.bsl_version.restype = i32
-    for name in ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_destroy"):
+    for name in ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_backward", "bsl_destroy"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -121,6 +122,12 @@ def bsl_forward_traced(plan, batch, n, q, k, v, o, seqlens, lse, active, masks, 
     _check(load().bsl_forward_traced(plan, batch, n, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                      _ptr(seqlens), _ptr(lse), _ptr(active), _ptr(masks),
                                      _stream(stream)))
+
+
+def bsl_backward(plan, batch, n, q, k, v, o, dout, lse, seqlens, dq, dk, dv, delta, stream=None):
+    _check(load().bsl_backward(plan, batch, n, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                               _ptr(lse), _ptr(seqlens), _ptr(dq), _ptr(dk), _ptr(dv),
+                               _ptr(delta), _stream(stream)))
 
 
 def bsl_destroy(plan):
@@ -197,3 +204,27 @@ class Plan:
         masks = torch.empty((batch, n // 32, w, 32), dtype=torch.int32, device=q.device)
         bsl_forward_traced(self.handle, batch, n, q, k, v, o, seqlens, lse, active, masks, stream)
         return o, active, masks
+
+    def backward(self, q, k, v, o, dout, lse, seqlens=None, dq=None, dk=None, dv=None,
+                 delta=None, stream=None):
+        """Returns (dq, dk, dv); see bsl_backward in include/bsl.h.  ``lse`` is the
+        one the forward wrote; ``delta`` (float32 [batch, heads, n]) is made here
+        when not given."""
+        import torch
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(q) if dk is None else dk
+        dv = torch.empty_like(q) if dv is None else dv
+        if delta is None:
+            delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        self._check_tensors(q, k, v, o, seqlens, lse)
+        for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+            if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous tensor like q")
+        if lse is None:
+            raise ValueError("the backward pass needs the lse the forward wrote")
+        if (delta.dtype != torch.float32 or delta.shape != q.shape[:3]
+                or not delta.is_contiguous()):
+            raise ValueError("delta must be a contiguous float32 tensor of shape [batch, heads, n]")
+        bsl_backward(self.handle, q.shape[0], q.shape[2], q, k, v, o, dout, lse, seqlens, dq, dk,
+                     dv, delta, stream)
+        return dq, dk, dv

@@ -103,6 +103,99 @@ bsl_status run(const bsl_plan *plan, int32_t batch, int32_t n, const void *q, co
     return BSL_OK;
 }
 
+bool overlaps(const void *a, size_t an, const void *b, size_t bn)
+{
+    const uint8_t *x = (const uint8_t *)a, *y = (const uint8_t *)b;
+    return x < y + bn && y < x + an;
+}
+
+bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
+                        const void *k, const void *v, const void *o, const void *dout,
+                        const float *lse, const int32_t *seqlens, void *dq, void *dk, void *dv,
+                        float *delta, void *stream)
+{
+    if (!plan)
+        return fail(BSL_E_INVALID, "plan is NULL");
+    const bsl_desc &d = plan->desc;
+    if (d.dtype != BSL_BF16)
+        return fail(BSL_E_UNSUPPORTED, "the backward pass is built for bf16 plans only");
+    if (d.head_dim != 64 && d.head_dim != 128)
+        return fail(BSL_E_UNSUPPORTED, "the backward pass supports head_dim 64 and 128 (got %d)",
+                    d.head_dim);
+    if (batch < 0 || n < 0)
+        return fail(BSL_E_INVALID, "batch (%d) and n (%d) must be >= 0", batch, n);
+    if (n % d.block_size != 0)
+        return fail(BSL_E_INVALID, "n (%d) is not a multiple of the block size %d", n,
+                    d.block_size);
+    if (batch == 0 || n == 0)
+        return BSL_OK;
+    const void *ins[] = {q, k, v, o, dout, lse};
+    void *outs[] = {dq, dk, dv, delta};
+    for (const void *x : ins)
+        if (!x)
+            return fail(BSL_E_INVALID, "q, k, v, o, dout and lse must be non-NULL device pointers");
+    for (const void *x : outs)
+        if (!x)
+            return fail(BSL_E_INVALID, "dq, dk, dv and delta must be non-NULL device pointers");
+    for (const void *x : ins)
+        if (!aligned16(x))
+            return fail(BSL_E_INVALID, "every tensor must be 16-byte aligned");
+    for (const void *x : outs)
+        if (!aligned16(x))
+            return fail(BSL_E_INVALID, "every tensor must be 16-byte aligned");
+    const long double elems = (long double)batch * d.heads * (long double)n * d.head_dim;
+    if (elems > 9.0e18L)
+        return fail(BSL_E_INVALID, "tensor of %d x %d x %d x %d elements is too large", batch,
+                    d.heads, n, d.head_dim);
+    const long long nblk = n / d.block_size;
+    if ((long long)batch * d.heads * nblk > 0x7fffffffLL ||
+        (long long)batch * d.heads * n > 0x7fffffffLL)
+        return fail(BSL_E_INVALID, "batch * heads * n exceeds 2^31 - 1");
+    const size_t tb = (size_t)elems * 2;                           // one bf16 tensor
+    const size_t rb = (size_t)batch * d.heads * (size_t)n * 4;     // one float row vector
+    const size_t in_bytes[] = {tb, tb, tb, tb, tb, rb};
+    const size_t out_bytes[] = {tb, tb, tb, rb};
+    for (int a = 0; a < 4; ++a) {
+        for (int b = 0; b < 6; ++b)
+            if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b]))
+                return fail(BSL_E_INVALID, "dq, dk, dv and delta must not overlap any input");
+        for (int b = a + 1; b < 4; ++b)
+            if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b]))
+                return fail(BSL_E_INVALID, "dq, dk, dv and delta must not overlap each other");
+    }
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return fail(BSL_E_DEVICE, "hipGetDevice failed");
+    if (dev != plan->device)
+        return fail(BSL_E_INVALID, "current device %d is not the plan's device %d", dev,
+                    plan->device);
+
+    bsl::BwdLaunch a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.seqlens = seqlens;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.delta = delta;
+    a.batch = batch;
+    a.heads = d.heads;
+    a.n = n;
+    a.head_dim = d.head_dim;
+    a.radius = d.radius;
+    a.causal = d.causal != 0;
+    a.scale = plan->scale;
+    a.stream = (hipStream_t)stream;
+    const hipError_t e = bsl::launch_bwd_bf16(a);
+    if (e != hipSuccess)
+        return fail(BSL_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    return BSL_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -163,6 +256,14 @@ bsl_status bsl_forward_traced(const bsl_plan *plan, int32_t batch, int32_t n, co
                               float *lse, int32_t *active, uint32_t *masks, void *stream)
 {
     return run(plan, batch, n, q, k, v, o, seqlens, lse, active, masks, stream, true);
+}
+
+bsl_status bsl_backward(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
+                        const void *k, const void *v, const void *o, const void *dout,
+                        const float *lse, const int32_t *seqlens, void *dq, void *dk, void *dv,
+                        float *delta, void *stream)
+{
+    return run_backward(plan, batch, n, q, k, v, o, dout, lse, seqlens, dq, dk, dv, delta, stream);
 }
 
 bsl_status bsl_destroy(bsl_plan *plan)

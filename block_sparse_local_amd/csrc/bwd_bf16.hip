@@ -1,0 +1,620 @@
+// bwd_bf16.hip -- backward pass of the banded block-sparse attention, bf16, gfx950.
+//
+// Method: NucleoByte project page, section 3, "Custom Backpropagation": with P
+// the forward's softmax, a per-row correction D_t = sum_c dO_tc O_tc and
+// dS_ts = P_ts (dO_t . V_s - D_t).  The gradients then follow by the chain
+// rule through S = scale Q K^T and O = P V:
+//     dV = P^T dO,   dQ = scale dS K,   dK = scale dS^T Q.
+// The band, padding and causal rules are the forward's (section 3, "Localized
+// Block-Sparse Attention Matrix"; section 2, item 2).  P is recomputed from the
+// scores and the forward's stored log-sum-exp: P = exp(S - lse).
+//
+// Three kernels, in stream order:
+//  * delta: D_t in fp32 from the bf16 O and dO; 0 on padded rows.
+//  * dq: one wave per query block, 4 per workgroup, sweeping the union of their
+//    key bands like the forward (ring of K/V blocks filled by direct-to-LDS
+//    loads, rotated sweep, XCD-contiguous groups).  Per key block
+//        S^T = K Q^T,  dP^T = V dO^T,  P^T = 2^(S^T c - lse log2 e),
+//        dS^T = P^T (dP^T - D),  dQ^T += K^T dS^T.
+//    As in the forward each lane owns one query column, so lse and D are
+//    per-lane scalars; dS^T enters the last product as the MFMA B operand
+//    straight from the accumulator, and K^T comes from transposing LDS reads.
+//  * dkv: one wave per key block, 4 per workgroup, sweeping the union of their
+//    query bands (ring of Q, dO, lse and D blocks).  Per query block
+//        S = Q K^T,  dP = dO V^T  (each lane owns one key column),
+//        dV^T += dO^T P,  dK^T += Q^T dS.
+// P and dS are rounded once to bf16 for the MFMAs; every sum is fp32.  K (in
+// dq) and Q, dO (in dkv) are read both row-wise and transposed, so their LDS
+// tiles use one swizzle that keeps both access patterns free of bank
+// conflicts.  Masks are applied by select, and rows past a sequence's end are
+// zeroed in LDS before any transposing read, so NaN padding cannot leak through
+// a zero probability.
+#include "cdna4.h"
+#include "launch.h"
+
+#include <math.h>
+
+namespace bsl {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// LDS tile of 32 rows x D bf16 for the backward kernels: row-major, 16-byte
+// chunk c of row r at chunk position c ^ swz(r).  Row reads take one chunk from
+// 16 consecutive rows; transposing reads take 4 consecutive rows x 4 chunks.
+// swz gives 16 consecutive rows 16 distinct positions (one per bank group of a
+// 256-byte window) and sends 4 consecutive rows to 4 different aligned 4-chunk
+// sets.  swz(r + 16) == swz(r) and swz(r + 8) == swz(r) ^ 2.
+template <int D>
+struct BTile {
+    static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+    static constexpr int CPR = D / 8;
+    static constexpr int BYTES = BLK * D * 2;
+    static constexpr int ROW_BYTES = D * 2;
+    __device__ static __forceinline__ int swz(int r)
+    {
+        if constexpr (D == 128)
+            return ((r & 3) << 2) | ((r >> 2) & 3);
+        else // two rows share a 256-byte window: swizzle by the row pair m = r / 2
+            return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    }
+};
+
+struct BParams {
+    const uint16_t *q, *k, *v, *o, *dout;
+    const float *lse;
+    const int32_t *seqlens;
+    uint16_t *dq, *dk, *dv;
+    float *delta;
+    int32_t heads, n, nblk, ngroups, radius, total;
+    float c;     // scale * log2(e)
+    float scale; // scale
+};
+
+__device__ __forceinline__ int seq_len(const BParams &p, int b)
+{
+    int len = p.seqlens ? p.seqlens[b] : p.n;
+    return len < 0 ? 0 : (len > p.n ? p.n : len);
+}
+
+// --------------------------------------------------------------- delta
+// D_t = sum_c dO_tc O_tc: D/8 lanes per row, 8 bf16 each, reduced by xor
+// shuffles; 0 on rows at or past the sequence's length.
+template <int D>
+__global__ void __launch_bounds__(256) delta_kernel(BParams p)
+{
+    constexpr int LPR = D / 8;           // lanes per row
+    constexpr int RPB = 256 / LPR;       // rows per workgroup
+    const int tid = threadIdx.x;
+    const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR; // over batch*heads*n
+    const int part = tid % LPR;
+    const int64_t rows = (int64_t)p.total; // batch * heads * n here
+    if (row >= rows)
+        return;
+    const int t = (int)(row % p.n);
+    const int b = (int)(row / p.n / p.heads);
+    const int len = seq_len(p, b);
+    float acc = 0.0f;
+    if (t < len) {
+        const u32x4 a = *(const u32x4 *)(p.dout + row * D + part * 8);
+        const u32x4 o = *(const u32x4 *)(p.o + row * D + part * 8);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, a), ov = __builtin_bit_cast(bf16x8, o);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc = fmaf((float)av[e], (float)ov[e], acc);
+    }
+#pragma unroll
+    for (int w = 1; w < LPR; w <<= 1)
+        acc += __shfl_xor(acc, w);
+    if (part == 0)
+        p.delta[row] = acc;
+}
+
+// ------------------------------------------------------------ shared parts
+// Band of block x (a query block for dq, a key block for dkv) within nb real
+// blocks: the blocks it pairs with.  For dq the partners are key blocks <= x
+// when causal; for dkv they are query blocks >= x.
+__device__ __forceinline__ void band_of(int x, int nb, int R, bool causal, bool partners_below,
+                                        int &lo, int &hi)
+{
+    lo = x - R < 0 ? 0 : x - R;
+    hi = x + R > nb - 1 ? nb - 1 : x + R;
+    if (causal) {
+        if (partners_below)
+            hi = hi > x ? x : hi;
+        else
+            lo = lo < x ? x : lo;
+    }
+}
+
+// Fill slot range of one 16 KB-or-8 KB tile pair in a ring stage: slot s of
+// the stage (16 bytes at stage + 16 s) holds tile A (s < SLOTS/2) or tile B.
+template <int D, int NT, int LPT>
+__device__ __forceinline__ void issue_pair(uint8_t *stage, const uint16_t *ga, const uint16_t *gb,
+                                          int row0, int tid, int wave)
+{
+    using T = BTile<D>;
+    constexpr int SLOTS = 2 * T::BYTES / 16;
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+        const int s = u * NT + tid;
+        const bool second = s >= SLOTS / 2;
+        const int t = second ? s - SLOTS / 2 : s;
+        const int r = t / T::CPR, cp = t % T::CPR;
+        const int c = cp ^ T::swz(r);
+        const uint16_t *src = (second ? gb : ga) + (size_t)(row0 + r) * D + c * 8;
+        uint8_t *dst = stage + (u * NT + wave * 64) * 16;
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
+    }
+}
+
+// Zero rows [r0, 32) of an LDS tile (whole rows: the swizzle does not matter).
+template <int D, int NT>
+__device__ __forceinline__ void zero_tail_rows(uint8_t *tile, int r0, int tid)
+{
+    using T = BTile<D>;
+    for (int x = tid; x < (BLK - r0) * T::CPR; x += NT)
+        *(u32x4 *)(tile + (r0 * T::CPR + x) * 16) = u32x4{0, 0, 0, 0};
+}
+
+// Row read of logical chunk `chunk` of row `row` (MFMA A operand fragment).
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const uint8_t *tile, int row, int chunk)
+{
+    using T = BTile<D>;
+    return as_bf16x8(*(const u32x4 *)(tile + row * T::ROW_BYTES + ((chunk ^ T::swz(row)) << 4)));
+}
+
+// The transposed operand of output tile m (32 columns of D) from an LDS tile:
+// two MFMA A fragments (keys or queries 0-15 and 16-31 in the accumulator's
+// permuted order).
+template <int D>
+__device__ __forceinline__ void tr_frags(const uint8_t *tile, int m, int tr_row, int tr_col,
+                                         bf16x8 &a0, bf16x8 &a1)
+{
+    using T = BTile<D>;
+    const int chunk = 4 * m + (tr_col >> 3);
+    const uint32_t base = (uint32_t)(size_t)(lds_u8 *)tile + (tr_col & 7) * 2;
+    const uint32_t a_r0 = base + tr_row * T::ROW_BYTES + ((chunk ^ T::swz(tr_row)) << 4);
+    const uint32_t a_r8 = base + (tr_row + 8) * T::ROW_BYTES + ((chunk ^ T::swz(tr_row + 8)) << 4);
+    u32x2 r0, r1, r2, r3;
+    tr_tile_2a<T::ROW_BYTES>(a_r0, a_r8, r0, r1, r2, r3);
+    const bf16x4 q0 = __builtin_bit_cast(bf16x4, r0), q1 = __builtin_bit_cast(bf16x4, r1);
+    const bf16x4 q2 = __builtin_bit_cast(bf16x4, r2), q3 = __builtin_bit_cast(bf16x4, r3);
+    a0 = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+    a1 = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Pack 16 fp32 accumulator values into the two bf16 B fragments of a product
+// that contracts over the accumulator's rows.
+__device__ __forceinline__ void pack_b(const float *x, bf16x8 &b0, bf16x8 &b1)
+{
+    uint32_t pk[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        pk[u] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[2 * u], x[2 * u + 1]}, bf16x2));
+    b0 = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+    b1 = as_bf16x8(u32x4{pk[4], pk[5], pk[6], pk[7]});
+}
+
+// Store a transposed fp32 accumulator (NMT tiles of 32 columns) as bf16 row
+// `row` of `out` (already offset to the slice), scaled; zeros when !valid.
+template <int NMT>
+__device__ __forceinline__ void store_rowT(uint16_t *out_row, const f32x16 *acc, float mul, bool valid,
+                                           int half)
+{
+#pragma unroll
+    for (int m = 0; m < NMT; ++m) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            f32x2 lo2 = {acc[m][4 * a] * mul, acc[m][4 * a + 1] * mul};
+            f32x2 hi2 = {acc[m][4 * a + 2] * mul, acc[m][4 * a + 3] * mul};
+            if (!valid) {
+                lo2 = f32x2{0.0f, 0.0f};
+                hi2 = f32x2{0.0f, 0.0f};
+            }
+            const u32x2 packed = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo2, bf16x2)),
+                                  __builtin_bit_cast(uint32_t, __builtin_convertvector(hi2, bf16x2))};
+            *(u32x2 *)(out_row + m * 32 + 8 * a + 4 * half) = packed;
+        }
+    }
+}
+
+// ------------------------------------------------------------------- dq
+template <int D, int NSTAGE, bool CAUSAL>
+__global__ void __launch_bounds__(256) dq_kernel(BParams p)
+{
+    using T = BTile<D>;
+    constexpr int MQ = 4, NT = 256;
+    constexpr int NMT = D / 32, NKS = D / 16;
+    constexpr int STAGE = 2 * T::BYTES; // K tile then V tile
+    constexpr int LPT = STAGE / 16 / NT;
+    static_assert(STAGE / 16 % NT == 0 && LPT >= 1, "slots split evenly over threads");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, half = lane >> 5;
+
+    const int g = xcd_contiguous((int)blockIdx.x, p.total);
+    const int grp = g % p.ngroups, bh = g / p.ngroups, b = bh / p.heads;
+    const int len = seq_len(p, b);
+    const int nb = (len + BLK - 1) / BLK;
+    const int R = p.radius;
+    const int i0 = grp * MQ, i = i0 + wave;
+    const bool exists = i < p.nblk;
+    const size_t base = (size_t)bh * (size_t)p.n * D;
+    const int qrow = i * BLK + col;
+    const bool qvalid = exists && qrow < len;
+    uint16_t *dq_row = p.dq + base + (size_t)qrow * D;
+
+    if (i0 >= nb) { // a group of padding only
+        if (exists)
+            for (int c = lane; c < BLK * D / 8; c += 64)
+                *(u32x4 *)(p.dq + base + (size_t)i * BLK * D + (size_t)c * 8) = u32x4{0, 0, 0, 0};
+        return;
+    }
+    int lo_w = 1, hi_w = 0;
+    if (exists && i < nb)
+        band_of(i, nb, R, CAUSAL, true, lo_w, hi_w);
+    const int jlo = i0 - R < 0 ? 0 : i0 - R;
+    int jhi = i0 + MQ - 1 + R > nb - 1 ? nb - 1 : i0 + MQ - 1 + R;
+    if (CAUSAL && jhi > i0 + MQ - 1)
+        jhi = i0 + MQ - 1;
+    const int L = jhi - jlo + 1;
+    const int P = CAUSAL ? MQ + R : MQ + 2 * R;
+    const int rot = L == P ? (P - jlo % P) % P : 0;
+    auto block_at = [&](int t) {
+        const int x = t + rot;
+        return jlo + (x >= L ? x - L : x);
+    };
+    const uint16_t *const kg = p.k + base, *const vg = p.v + base;
+    auto issue = [&](int j, int stage) {
+        issue_pair<D, NT, LPT>(lds + stage * STAGE, kg, vg, j * BLK, tid, wave);
+    };
+
+    // this wave's query fragments, lse (log2 units) and D
+    bf16x8 qf[NKS], gf[NKS];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+        u32x4 x = u32x4{0, 0, 0, 0}, y = u32x4{0, 0, 0, 0};
+        if (qvalid) {
+            x = *(const u32x4 *)(p.q + base + (size_t)qrow * D + s * 16 + half * 8);
+            y = *(const u32x4 *)(p.dout + base + (size_t)qrow * D + s * 16 + half * 8);
+        }
+        qf[s] = as_bf16x8(x);
+        gf[s] = as_bf16x8(y);
+    }
+    const float lse2 = qvalid ? p.lse[(size_t)bh * p.n + qrow] * LOG2E : 0.0f;
+    const float Dt = qvalid ? p.delta[(size_t)bh * p.n + qrow] : 0.0f;
+
+#pragma unroll
+    for (int a = 0; a < NSTAGE - 1; ++a)
+        if (a < L)
+            issue(block_at(a), a);
+
+    f32x16 acc[NMT];
+#pragma unroll
+    for (int m = 0; m < NMT; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            acc[m][r] = 0.0f;
+
+    const int grp16 = lane >> 4, li = lane & 15;
+    const int tr_row = 4 * half + (li >> 2);
+    const int tr_col = 16 * (grp16 & 1) + 4 * (li & 3);
+
+    for (int t = 0; t < L; ++t) {
+        const int j = block_at(t);
+        const int stage = t % NSTAGE;
+        if (t + NSTAGE - 2 < L)
+            wait_vm_lgkm0<(NSTAGE - 2) * LPT>();
+        else
+            wait_vm_lgkm0<0>();
+        workgroup_barrier();
+        if (t + NSTAGE - 1 < L)
+            issue(block_at(t + NSTAGE - 1), (t + NSTAGE - 1) % NSTAGE);
+        uint8_t *kl = lds + stage * STAGE;
+        const uint8_t *vl = kl + T::BYTES;
+        const bool pad_block = j == nb - 1 && (len & (BLK - 1)) != 0;
+        if (pad_block) {
+            // K rows past the end enter the transposed product: make them 0
+            zero_tail_rows<D, NT>(kl, len - j * BLK, tid);
+            wait_vm_lgkm0<63>();
+            workgroup_barrier();
+        }
+        if (j < lo_w || j > hi_w)
+            continue;
+
+        f32x16 s, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s[r] = 0.0f;
+            dp[r] = 0.0f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const bf16x8 ka = row_frag<D>(kl, col, 2 * ks + half);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const bf16x8 va = row_frag<D>(vl, col, 2 * ks + half);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], dp, 0, 0, 0);
+        }
+        const bool need_mask = !qvalid || pad_block || (CAUSAL && j == i);
+        float ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -lse2));
+            ds[r] = pr * (dp[r] - Dt);
+        }
+        if (need_mask) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = j * BLK + acc_row(r, half);
+                const bool keep = qvalid && key < len && (!CAUSAL || key <= qrow);
+                ds[r] = keep ? ds[r] : 0.0f;
+            }
+        }
+        bf16x8 db0, db1;
+        pack_b(ds, db0, db1);
+#pragma unroll
+        for (int m = 0; m < NMT; ++m) {
+            bf16x8 a0, a1;
+            tr_frags<D>(kl, m, tr_row, tr_col, a0, a1);
+            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, db0, acc[m], 0, 0, 0);
+            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, db1, acc[m], 0, 0, 0);
+        }
+    }
+    if (exists)
+        store_rowT<NMT>(dq_row, acc, p.scale, qvalid, half);
+}
+
+// ------------------------------------------------------------------ dkv
+template <int D, int NSTAGE, bool CAUSAL>
+__global__ void __launch_bounds__(256) dkv_kernel(BParams p)
+{
+    using T = BTile<D>;
+    constexpr int MK = 4, NT = 256;
+    constexpr int NMT = D / 32, NKS = D / 16;
+    constexpr int TILES = 2 * T::BYTES;      // Q tile then dO tile
+    constexpr int STAGE = TILES + 2 * BLK * 4; // then lse[32], D[32]
+    constexpr int LPT = TILES / 16 / NT;
+    static_assert(TILES / 16 % NT == 0 && LPT >= 1, "slots split evenly over threads");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, half = lane >> 5;
+
+    const int g = xcd_contiguous((int)blockIdx.x, p.total);
+    const int grp = g % p.ngroups, bh = g / p.ngroups, b = bh / p.heads;
+    const int len = seq_len(p, b);
+    const int nb = (len + BLK - 1) / BLK;
+    const int R = p.radius;
+    const int j0 = grp * MK, j = j0 + wave;
+    const bool exists = j < p.nblk;
+    const size_t base = (size_t)bh * (size_t)p.n * D;
+    const size_t rbase = (size_t)bh * (size_t)p.n; // lse, delta
+    const int krow = j * BLK + col;
+    const bool kvalid = exists && krow < len;
+    uint16_t *dk_row = p.dk + base + (size_t)krow * D;
+    uint16_t *dv_row = p.dv + base + (size_t)krow * D;
+
+    if (j0 >= nb) {
+        if (exists)
+            for (int c = lane; c < BLK * D / 8; c += 64) {
+                const size_t off = base + (size_t)j * BLK * D + (size_t)c * 8;
+                *(u32x4 *)(p.dk + off) = u32x4{0, 0, 0, 0};
+                *(u32x4 *)(p.dv + off) = u32x4{0, 0, 0, 0};
+            }
+        return;
+    }
+    int lo_w = 1, hi_w = 0;
+    if (exists && j < nb)
+        band_of(j, nb, R, CAUSAL, false, lo_w, hi_w);
+    const int ilo = CAUSAL ? j0 : (j0 - R < 0 ? 0 : j0 - R);
+    const int ihi = j0 + MK - 1 + R > nb - 1 ? nb - 1 : j0 + MK - 1 + R;
+    const int L = ihi - ilo + 1;
+    const int P = CAUSAL ? MK + R : MK + 2 * R;
+    const int rot = L == P ? (P - ilo % P) % P : 0;
+    auto block_at = [&](int t) {
+        const int x = t + rot;
+        return ilo + (x >= L ? x - L : x);
+    };
+    // Q and dO tiles by every thread; lse and D (32 floats each) by lanes 0-15
+    // of wave 0, which therefore has one more load in flight per stage
+    const uint16_t *const qg = p.q + base, *const gg = p.dout + base;
+    const float *const lg = p.lse + rbase, *const dg = p.delta + rbase;
+    auto issue = [&](int i, int stage) {
+        uint8_t *st = lds + stage * STAGE;
+        issue_pair<D, NT, LPT>(st, qg, gg, i * BLK, tid, wave);
+        if (wave == 0 && lane < 16) {
+            const float *src = (lane < 8 ? lg : dg) + i * BLK + (lane & 7) * 4;
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(st + TILES), 16, 0, 0);
+        }
+    };
+
+    // this wave's key and value fragments (B operands of S = Q K^T, dP = dO V^T)
+    bf16x8 kf[NKS], vf[NKS];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+        u32x4 x = u32x4{0, 0, 0, 0}, y = u32x4{0, 0, 0, 0};
+        if (kvalid) {
+            x = *(const u32x4 *)(p.k + base + (size_t)krow * D + s * 16 + half * 8);
+            y = *(const u32x4 *)(p.v + base + (size_t)krow * D + s * 16 + half * 8);
+        }
+        kf[s] = as_bf16x8(x);
+        vf[s] = as_bf16x8(y);
+    }
+
+#pragma unroll
+    for (int a = 0; a < NSTAGE - 1; ++a)
+        if (a < L)
+            issue(block_at(a), a);
+
+    f32x16 dka[NMT], dva[NMT];
+#pragma unroll
+    for (int m = 0; m < NMT; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            dka[m][r] = 0.0f;
+            dva[m][r] = 0.0f;
+        }
+
+    const int grp16 = lane >> 4, li = lane & 15;
+    const int tr_row = 4 * half + (li >> 2);
+    const int tr_col = 16 * (grp16 & 1) + 4 * (li & 3);
+    const float c = p.c;
+
+    for (int t = 0; t < L; ++t) {
+        const int i = block_at(t);
+        const int stage = t % NSTAGE;
+        if (t + NSTAGE - 2 < L) {
+            if (wave == 0)
+                wait_vm_lgkm0<(NSTAGE - 2) * (LPT + 1)>();
+            else
+                wait_vm_lgkm0<(NSTAGE - 2) * LPT>();
+        } else {
+            wait_vm_lgkm0<0>();
+        }
+        workgroup_barrier();
+        if (t + NSTAGE - 1 < L)
+            issue(block_at(t + NSTAGE - 1), (t + NSTAGE - 1) % NSTAGE);
+        uint8_t *ql = lds + stage * STAGE;
+        uint8_t *gl = ql + T::BYTES;
+        const float *lsel = (const float *)(ql + TILES);
+        const float *dl = lsel + BLK;
+        const bool pad_block = i == nb - 1 && (len & (BLK - 1)) != 0;
+        if (pad_block) {
+            // Q and dO rows past the end enter the transposed products: make them 0
+            zero_tail_rows<D, NT>(ql, len - i * BLK, tid);
+            zero_tail_rows<D, NT>(gl, len - i * BLK, tid);
+            wait_vm_lgkm0<63>();
+            workgroup_barrier();
+        }
+        if (i < lo_w || i > hi_w)
+            continue;
+
+        f32x16 s, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s[r] = 0.0f;
+            dp[r] = 0.0f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const bf16x8 qa = row_frag<D>(ql, col, 2 * ks + half);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const bf16x8 ga = row_frag<D>(gl, col, 2 * ks + half);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
+        }
+        // lse and D of this lane's 16 query rows: rows 8a + 4 half + (0..3)
+        f32x4 l4[4], d4[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            l4[a] = *(const f32x4 *)(lsel + 8 * a + 4 * half);
+            d4[a] = *(const f32x4 *)(dl + 8 * a + 4 * half);
+        }
+        const bool need_mask = !kvalid || pad_block || (CAUSAL && i == j);
+        float pv[16], ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float lr = l4[r >> 2][r & 3], dr = d4[r >> 2][r & 3];
+            const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lr * LOG2E));
+            pv[r] = pr;
+            ds[r] = pr * (dp[r] - dr);
+        }
+        if (need_mask) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qr = i * BLK + acc_row(r, half);
+                const bool keep = kvalid && qr < len && (!CAUSAL || krow <= qr);
+                pv[r] = keep ? pv[r] : 0.0f;
+                ds[r] = keep ? ds[r] : 0.0f;
+            }
+        }
+        bf16x8 pb0, pb1, db0, db1;
+        pack_b(pv, pb0, pb1);
+        pack_b(ds, db0, db1);
+#pragma unroll
+        for (int m = 0; m < NMT; ++m) {
+            bf16x8 a0, a1;
+            tr_frags<D>(gl, m, tr_row, tr_col, a0, a1);
+            dva[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, pb0, dva[m], 0, 0, 0);
+            dva[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, pb1, dva[m], 0, 0, 0);
+        }
+#pragma unroll
+        for (int m = 0; m < NMT; ++m) {
+            bf16x8 a0, a1;
+            tr_frags<D>(ql, m, tr_row, tr_col, a0, a1);
+            dka[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, db0, dka[m], 0, 0, 0);
+            dka[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, db1, dka[m], 0, 0, 0);
+        }
+    }
+    if (exists) {
+        store_rowT<NMT>(dk_row, dka, p.scale, kvalid, half);
+        store_rowT<NMT>(dv_row, dva, 1.0f, kvalid, half);
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_d(const BwdLaunch &a, BParams p)
+{
+    constexpr int NS = 3;
+    // delta over every row of every (batch, head)
+    BParams pd = p;
+    const int64_t rows = (int64_t)a.batch * a.heads * a.n;
+    pd.total = (int32_t)rows;
+    constexpr int RPB = 256 / (D / 8);
+    const int64_t dblocks = (rows + RPB - 1) / RPB;
+    hipLaunchKernelGGL((delta_kernel<D>), dim3((unsigned)dblocks), dim3(256), 0, a.stream, pd);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((dq_kernel<D, NS, CAUSAL>), dim3(p.total), dim3(256), 0, a.stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((dkv_kernel<D, NS, CAUSAL>), dim3(p.total), dim3(256), 0, a.stream, p);
+    return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_bwd_bf16(const BwdLaunch &a)
+{
+    BParams p;
+    p.q = (const uint16_t *)a.q;
+    p.k = (const uint16_t *)a.k;
+    p.v = (const uint16_t *)a.v;
+    p.o = (const uint16_t *)a.o;
+    p.dout = (const uint16_t *)a.dout;
+    p.lse = a.lse;
+    p.seqlens = a.seqlens;
+    p.dq = (uint16_t *)a.dq;
+    p.dk = (uint16_t *)a.dk;
+    p.dv = (uint16_t *)a.dv;
+    p.delta = a.delta;
+    p.heads = a.heads;
+    p.n = a.n;
+    p.nblk = a.n / BLK;
+    p.ngroups = (p.nblk + 3) / 4;
+    p.radius = a.radius;
+    p.total = a.batch * a.heads * p.ngroups;
+    p.c = a.scale * LOG2E;
+    p.scale = a.scale;
+    switch (a.head_dim) {
+    case 64: return a.causal ? launch_bwd_d<64, true>(a, p) : launch_bwd_d<64, false>(a, p);
+    case 128: return a.causal ? launch_bwd_d<128, true>(a, p) : launch_bwd_d<128, false>(a, p);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+} // namespace bsl

@@ -25,3 +25,22 @@ hipError_t launch_fwd_bf16(const Launch &a);
 hipError_t launch_fwd_f32(const Launch &a);
 
 } // namespace bsl
+
+namespace bsl {
+
+// One backward call, after argument validation.
+struct BwdLaunch {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    const int32_t *seqlens;
+    void *dq, *dk, *dv;
+    float *delta; // caller's workspace, [batch][heads][n]
+    int32_t batch, heads, n, head_dim, radius;
+    bool causal;
+    float scale;
+    hipStream_t stream;
+};
+
+hipError_t launch_bwd_bf16(const BwdLaunch &a);
+
+} // namespace bsl

@@ -7,7 +7,8 @@ needed to exercise the attention forward: Q, K, V are activations, replaced here
 by normal draws of the shapes and scales below.
 
 Recipe (also in DESIGN.md):
-  * every [n, d] slice (tensor t in {Q=0, K=1, V=2}, sequence b, head h) has its
+  * every [n, d] slice (tensor t in {Q=0, K=1, V=2, dO=3}, sequence b, head h; dO
+    is the output gradient the backward pass takes) has its
     own PCG64 stream ``numpy.random.default_rng([seed, cfg, t, b, h])``, so the
     values do not depend on the order of generation or on the batch order;
   * values are ``standard_normal(float32) * sigma``, then rounded to bf16
@@ -16,8 +17,8 @@ Recipe (also in DESIGN.md):
     uniformly in [500, 2048] and pads the buffer up to a multiple of 32;
   * the million-token workload samples 64 query blocks with
     ``default_rng([seed, 5, 4]).choice(nblk, 64, replace=False)``, sorted;
-  * with ``poison=True`` every padded row (t >= len_b) of Q, K and V is NaN, so a
-    kernel that reads padding shows it.
+  * with ``poison=True`` every padded row (t >= len_b) of Q, K, V (and dO) is
+    NaN, so a kernel that reads padding shows it.
 """
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
@@ -98,9 +99,10 @@ def _slice(seed, cfg, t, b, h, n, d, sigma, bf16):
 
 
 def draw(seed, cfg, batch, heads, n, d, sigma=1.0, bf16=True, seqlens=None, poison=False,
-         threads=None):
-    """(q, k, v) float32 [batch, heads, n, d] from the per-slice streams above."""
-    out = [np.empty((batch, heads, n, d), dtype=np.float32) for _ in range(3)]
+         threads=None, tensors=3):
+    """(q, k, v) float32 [batch, heads, n, d] from the per-slice streams above;
+    with tensors=4 also the output gradient dO (tensor index 3)."""
+    out = [np.empty((batch, heads, n, d), dtype=np.float32) for _ in range(tensors)]
 
     def fill(job):
         t, b, h = job
@@ -108,7 +110,7 @@ def draw(seed, cfg, batch, heads, n, d, sigma=1.0, bf16=True, seqlens=None, pois
         if poison and seqlens is not None and seqlens[b] < n:
             out[t][b, h, seqlens[b]:, :] = np.nan
 
-    jobs = [(t, b, h) for t in range(3) for b in range(batch) for h in range(heads)]
+    jobs = [(t, b, h) for t in range(tensors) for b in range(batch) for h in range(heads)]
     nthr = threads or min(16, len(os.sched_getaffinity(0)))
     if len(jobs) == 1 or nthr == 1:
         for j in jobs:
@@ -119,14 +121,19 @@ def draw(seed, cfg, batch, heads, n, d, sigma=1.0, bf16=True, seqlens=None, pois
     return tuple(out)
 
 
-def make(key: str, seed: int = 42, poison: bool = False, heads=None, n=None):
-    """Inputs of a named workload: dict(q, k, v, seqlens, n, workload).  ``heads``
-    and ``n`` shrink a workload for quick runs (lengths are clipped to n)."""
+def make(key: str, seed: int = 42, poison: bool = False, heads=None, n=None, grad=False):
+    """Inputs of a named workload: dict(q, k, v, seqlens, n, workload), plus
+    ``dout`` with grad=True.  ``heads`` and ``n`` shrink a workload for quick
+    runs (lengths are clipped to n)."""
     w = WORKLOADS[key]
     lens, nbuf = lengths(w, seed)
     if n is not None:
         nbuf = n
         lens = np.minimum(lens, n).astype(np.int32)
     hh = heads or w.heads
-    q, k, v = draw(seed, w.cfg, w.batch, hh, nbuf, w.d, w.sigma, w.dtype == "bf16", lens, poison)
-    return dict(q=q, k=k, v=v, seqlens=lens, n=nbuf, workload=w, heads=hh)
+    t = draw(seed, w.cfg, w.batch, hh, nbuf, w.d, w.sigma, w.dtype == "bf16", lens, poison,
+             tensors=4 if grad else 3)
+    out = dict(q=t[0], k=t[1], v=t[2], seqlens=lens, n=nbuf, workload=w, heads=hh)
+    if grad:
+        out["dout"] = t[3]
+    return out

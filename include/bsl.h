@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define BSL_VERSION 10000 /* major * 10000 + minor * 100 + patch */
+#define BSL_VERSION 10100 /* major * 10000 + minor * 100 + patch */
 
 typedef enum bsl_status {
     BSL_OK = 0,
@@ -109,6 +109,32 @@ bsl_status bsl_forward(const bsl_plan *plan, int32_t batch, int32_t n, const voi
 bsl_status bsl_forward_traced(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
                               const void *k, const void *v, void *o, const int32_t *seqlens,
                               float *lse, int32_t *active, uint32_t *masks, void *stream);
+
+/* Enqueue the backward pass of bsl_forward (NucleoByte project page, section 3,
+ * "Custom Backpropagation"): from the output gradient dO, the gradients dQ, dK,
+ * dV of the same loss.  With P the forward's softmax over each row's kept keys,
+ *   D_t = sum_c dO_tc O_tc,   dS_ts = P_ts (dO_t . V_s - D_t),
+ *   dV = P^T dO,   dQ = scale dS K,   dK = scale dS^T Q,
+ * and zero gradient on padded rows and keys.  bf16 plans with head_dim 64 or
+ * 128 only.
+ *   batch, n, seqlens, stream  as in bsl_forward (the same values it was given).
+ *   q, k, v  the forward's inputs; o its output, exactly as bsl_forward wrote it.
+ *   dout     device bf16 [batch][heads][n][head_dim]: the loss gradient w.r.t. o.
+ *            Rows past a sequence's length are ignored.
+ *   lse      device float[batch][heads][n]: the lse bsl_forward wrote.
+ *   dq, dk, dv  device bf16, same shape as q; every element is written.
+ *   delta    device float[batch][heads][n], a workspace the caller owns: the
+ *            call overwrites it with D (0 on padded rows).  The library
+ *            allocates nothing.
+ * All tensors 16-byte aligned.  dq, dk, dv and delta must not overlap each
+ * other or any input.  Returns BSL_E_UNSUPPORTED for an fp32 plan or head_dim
+ * 32, BSL_E_INVALID for the argument errors bsl_forward rejects, a NULL
+ * pointer, misalignment or overlap, and BSL_E_DEVICE if a launch fails.
+ * Nothing is written when an argument error is returned. */
+bsl_status bsl_backward(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
+                        const void *k, const void *v, const void *o, const void *dout,
+                        const float *lse, const int32_t *seqlens, void *dq, void *dk, void *dv,
+                        float *delta, void *stream);
 
 /* Release a plan.  NULL is accepted and ignored.  Do not call while work
  * enqueued with the plan is being launched from another thread. */

@@ -1,0 +1,179 @@
+"""GPU parity of the backward pass: bsl_backward (through the C ABI) against the
+fp64 oracle's gradients (NucleoByte project page, section 3, "Custom
+Backpropagation"; oracle pinned in test_oracle_backward.py).
+
+The GPU forward runs first and its bf16 O and lse feed the backward, as in
+training.  Padded rows of Q, K, V and dO hold NaN and every output starts as
+NaN, so a kernel that reads padding or skips an element fails.
+
+Tolerance (derivation in the design doc): the kernels round P and dS to bf16
+(relative 2^-9) before the products and take D from the bf16 O, so each
+gradient element carries a relative error of a few 2^-9 of the terms it sums.
+The bar is max-abs <= 2e-2 * s and mean-abs <= 2e-3 * s, with s the root mean
+square of the reference gradient over valid rows (at least 1): the forward's
+bars, measured in units of the gradient's own size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_local_amd import bsl, inputs
+from tests._gpu import dev, host, lens_dev, say
+
+pytestmark = pytest.mark.gpu
+
+MAX_TOL, MEAN_TOL = 2e-2, 2e-3
+
+
+def _gpu_backward(d, heads, dd, radius, causal):
+    q, k, v, g = (dev(d[x], "bf16") for x in ("q", "k", "v", "dout"))
+    sl = lens_dev(d["seqlens"])
+    plan = bsl.Plan(head_dim=dd, heads=heads, radius=radius, causal=causal)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    plan.forward(q, k, v, sl, o=o, lse=lse)
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    delta = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    plan.backward(q, k, v, o, g, lse, sl, dq=dq, dk=dk, dv=dv, delta=delta)
+    torch.cuda.synchronize()
+    out = dict(dq=host(dq), dk=host(dk), dv=host(dv), delta=delta.cpu().numpy(), o=host(o))
+    plan.close()
+    return out
+
+
+def _compare(name, got, ref, lens):
+    """Valid rows within the bar, padded rows exactly zero."""
+    errs, refs = [], []
+    for b, L in enumerate(lens):
+        L = int(L)
+        assert np.all(got[b, :, L:] == 0.0), f"{name}: padded rows of sequence {b} are not zero"
+        if L:
+            errs.append(np.abs(got[b, :, :L].astype(np.float64) - ref[b, :, :L]).ravel())
+            refs.append(ref[b, :, :L].ravel())
+    if not errs:
+        return
+    e, r = np.concatenate(errs), np.concatenate(refs)
+    assert np.all(np.isfinite(e)), f"{name}: non-finite values"
+    s = max(1.0, float(np.sqrt(np.mean(r * r))))
+    say(f"  {name}: max-abs {e.max():.3e} mean-abs {e.mean():.3e} (ref rms {s:.3g}, "
+        f"max |ref| {np.abs(r).max():.3g})")
+    assert e.max() <= MAX_TOL * s, f"{name}: max-abs {e.max()} > {MAX_TOL * s}"
+    assert e.mean() <= MEAN_TOL * s, f"{name}: mean-abs {e.mean()} > {MEAN_TOL * s}"
+
+
+def _case(batch, heads, n, dd, radius, causal, lens, seed, sigma=1.0):
+    lens = np.array(lens, dtype=np.int32)
+    q, k, v, g = inputs.draw(seed, 90, batch, heads, n, dd, sigma, True, lens, poison=True,
+                             tensors=4)
+    return dict(q=q, k=k, v=v, dout=g, seqlens=lens, n=n)
+
+
+CASES = [
+    # batch, heads, n, d, radius, causal, lens
+    (2, 2, 256, 64, 1, False, [256, 150]),
+    (2, 2, 256, 128, 2, True, [256, 61]),
+    (2, 2, 256, 64, 0, False, [256, 33]),
+    (1, 2, 96, 128, 3, False, [96]),          # radius past the last block: dense
+    (3, 1, 224, 64, 1, True, [0, 1, 200]),    # empty and one-token sequences
+    (2, 2, 320, 128, 1, False, [320, 289]),
+    (1, 3, 512, 64, 4, True, [512]),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_backward_small(case):
+    batch, heads, n, dd, radius, causal, lens = case
+    say(f"[backward] b{batch} h{heads} n{n} d{dd} R{radius} causal{int(causal)} lens {lens}")
+    d = _case(batch, heads, n, dd, radius, causal, lens, seed=len(lens) * 7 + dd + radius)
+    res = _gpu_backward(d, heads, dd, radius, causal)
+    dq, dk, dv = oracle.backward(d["q"], d["k"], d["v"], d["dout"], d["seqlens"], 32, radius,
+                                 causal)
+    _compare("dq", res["dq"], dq, d["seqlens"])
+    _compare("dk", res["dk"], dk, d["seqlens"])
+    _compare("dv", res["dv"], dv, d["seqlens"])
+    # D = dO . O on valid rows (O the GPU's bf16 output), 0 on padded rows
+    for b, L in enumerate(d["seqlens"]):
+        assert np.all(res["delta"][b, :, L:] == 0.0)
+        ref = np.einsum("hnd,hnd->hn", d["dout"][b, :, :L].astype(np.float64),
+                        res["o"][b, :, :L].astype(np.float64))
+        assert np.max(np.abs(res["delta"][b, :, :L] - ref), initial=0.0) <= 1e-3 * max(
+            1.0, np.abs(ref).max(initial=0.0))
+
+
+def test_backward_c3_reduced():
+    """The causal long-context workload's shape per head (R 4, d 64, sigma 0.5)."""
+    say("[backward] c3 reduced to 4 heads")
+    d = inputs.make("c3", 42, poison=True, heads=4, grad=True)
+    w = d["workload"]
+    d = dict(q=d["q"][:1], k=d["k"][:1], v=d["v"][:1], dout=d["dout"][:1],
+             seqlens=d["seqlens"][:1], n=d["n"])
+    res = _gpu_backward(d, 4, w.d, w.radius, w.causal)
+    dq, dk, dv = oracle.backward(d["q"], d["k"], d["v"], d["dout"], d["seqlens"], 32, w.radius,
+                                 w.causal)
+    for name, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _compare(name, res[name], ref, d["seqlens"])
+
+
+@pytest.mark.parametrize("key", ["c4", "c5"])
+def test_backward_full_size_sampled(key):
+    """Full-size backward; the oracle checks sampled blocks (dQ of query block i,
+    dK and dV of key block i) on every head."""
+    say(f"[backward] {key} full size")
+    d = inputs.make(key, 42, poison=True, grad=True)
+    w = d["workload"]
+    n = d["n"]
+    nblk = n // 32
+    L = int(d["seqlens"][0])
+    nb = (L + 31) // 32
+    rng = np.random.default_rng([42, w.cfg, 6])
+    blocks = sorted({0, 1, nb - 2, nb - 1, nb, nblk - 1} & set(range(nblk))
+                    | set(int(x) for x in rng.choice(nblk, 10, replace=False)))
+    res = _gpu_backward(d, w.heads, w.d, w.radius, w.causal)
+    sel = np.array([(0, h, i) for h in range(w.heads) for i in blocks], dtype=np.int32)
+    bq, bk, bv = oracle.backward_blocks(d["q"], d["k"], d["v"], d["dout"], sel, d["seqlens"], 32,
+                                        w.radius, w.causal)
+    rows = np.array([[i * 32 + r for r in range(32)] for _, _, i in sel])
+    valid = rows < L
+    for name, ref in (("dq", bq), ("dk", bk), ("dv", bv)):
+        got = np.stack([res[name][b, h, i * 32:(i + 1) * 32] for b, h, i in sel])
+        assert np.all(got[~valid] == 0.0), f"{name}: padded rows not zero"
+        e = np.abs(got[valid].astype(np.float64) - ref[valid])
+        r = ref[valid]
+        s = max(1.0, float(np.sqrt(np.mean(r * r))))
+        say(f"  {key} {name} sampled {len(sel)} blocks: max-abs {e.max():.3e} "
+            f"mean-abs {e.mean():.3e} (ref rms {s:.3g})")
+        assert np.all(np.isfinite(e))
+        assert e.max() <= MAX_TOL * s and e.mean() <= MEAN_TOL * s
+
+
+def test_backward_rejects_bad_arguments():
+    plan = bsl.Plan(head_dim=64, heads=1, radius=1)
+    t = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((1, 1, 64), dtype=torch.float32, device="cuda")
+    outs = [torch.zeros_like(t) for _ in range(3)]
+    delta = torch.zeros_like(lse)
+    with pytest.raises(bsl.BslError) as e:   # dq aliases q
+        bsl.bsl_backward(plan.handle, 1, 64, t, t, t, t, t, lse, None, t, outs[1], outs[2], delta)
+    assert e.value.status == bsl.BSL_E_INVALID
+    with pytest.raises(bsl.BslError) as e:   # n not a multiple of 32
+        bsl.bsl_backward(plan.handle, 1, 48, t, t, t, t, t, lse, None, *outs, delta)
+    assert e.value.status == bsl.BSL_E_INVALID
+    with pytest.raises(bsl.BslError) as e:   # missing workspace
+        bsl.bsl_backward(plan.handle, 1, 64, t, t, t, t, t, lse, None, *outs, None)
+    assert e.value.status == bsl.BSL_E_INVALID
+    plan.close()
+    p32 = bsl.Plan(head_dim=32, heads=1, radius=1)
+    t32 = torch.zeros((1, 1, 64, 32), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(bsl.BslError) as e:
+        bsl.bsl_backward(p32.handle, 1, 64, t32, t32, t32, t32, t32, lse, None,
+                         *[torch.zeros_like(t32) for _ in range(3)], delta)
+    assert e.value.status == bsl.BSL_E_UNSUPPORTED
+    p32.close()
+    pf = bsl.Plan(head_dim=64, heads=1, radius=1, dtype="f32")
+    tf = torch.zeros((1, 1, 64, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(bsl.BslError) as e:
+        bsl.bsl_backward(pf.handle, 1, 64, tf, tf, tf, tf, tf, lse, None,
+                         *[torch.zeros_like(tf) for _ in range(3)], delta)
+    assert e.value.status == bsl.BSL_E_UNSUPPORTED
+    pf.close()
