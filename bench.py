@@ -153,6 +153,73 @@ def time_workload(key, steps, warmup, cold=False, log=print):
     return dict(key=key, w=w, d=d, acc=acc, wall=wall, per_launch=per_launch, steps=steps)
 
 
+def time_backward(key, steps, warmup, log=print):
+    """The backward pass (bsl_backward) on the workload's inputs and a seeded
+    output gradient, after one forward that supplies O and lse."""
+    import torch
+    from block_sparse_local_amd import bsl, inputs, workload
+
+    d = inputs.make(key, 42, grad=True)
+    w = d["workload"]
+    lens = d["seqlens"]
+    q, k, v, g = (to_device(d[x], w.dtype) for x in ("q", "k", "v", "dout"))
+    sl = torch.from_numpy(lens).cuda()
+    plan = bsl.Plan(w.d, w.heads, w.radius, w.causal, w.dtype)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    plan.forward(q, k, v, sl, o=o, lse=lse, stream=stream)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    delta = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    acc = workload.account_backward(lens, w.heads, w.d, w.radius, w.causal, w.dtype)
+    for _ in range(warmup):
+        plan.backward(q, k, v, o, g, lse, sl, dq=dq, dk=dk, dv=dv, delta=delta, stream=stream)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t_begin = time.perf_counter()
+    for s in range(steps):
+        starts[s].record(stream)
+        plan.backward(q, k, v, o, g, lse, sl, dq=dq, dk=dk, dv=dv, delta=delta, stream=stream)
+        ends[s].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_begin
+    per_launch = np.array([a.elapsed_time(b) * 1e-3 for a, b in zip(starts, ends)])
+    plan.close()
+    del q, k, v, g, o, lse, dq, dk, dv, delta
+    torch.cuda.empty_cache()
+    log(f"[bench] {key} backward: {wall / steps * 1e3:.3f} ms/step")
+    return dict(key=key, w=w, d=d, acc=acc, wall=wall, per_launch=per_launch, steps=steps)
+
+
+def cpu_baseline_backward(r, target_flops=6.0e11, log=print):
+    """The fp64 oracle's backward on every head of the first tokens of the
+    workload's first sequence (a bounded sample of the same shape, about
+    ``target_flops`` useful FLOP)."""
+    import oracle
+    from block_sparse_local_amd import workload
+    d, w = r["d"], r["w"]
+    per_token = 10.0 * w.d * (2 * w.radius + 1) * 32 * w.heads
+    rows = max(32, int(target_flops / per_token) // 32 * 32)
+    L = min(rows, int(d["seqlens"][0]))
+    n = -(-L // 32) * 32
+    sl = lambda x: np.ascontiguousarray(x[:1, :, :n])
+    lens = np.array([L], dtype=np.int32)
+    threads = min(16, oracle.default_threads())
+    t0 = time.perf_counter()
+    oracle.backward(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["dout"]), lens, 32, w.radius,
+                    w.causal, nthreads=threads)
+    dt = time.perf_counter() - t0
+    acc = workload.account_backward(lens, w.heads, w.d, w.radius, w.causal, w.dtype)
+    log(f"[bench] oracle backward: {w.heads} heads x {L} tokens in {dt:.1f}s")
+    return {"value": acc["useful_flops"] / dt / 1e12, "unit": "TFLOP/s",
+            "cores": min(threads, w.heads), "kind": "oracle",
+            "sample": f"backward of all {w.heads} heads over the first {L} tokens of sequence 0 "
+                      f"(one thread per head); {acc['useful_flops'] / 1e9:.1f} useful GFLOP in "
+                      f"{dt:.2f}s",
+            "seconds": dt}
+
+
 def cpu_baseline(r, target_flops=1.0e12, log=print):
     """Time the fp64 oracle on a bounded, evenly spread sample of query blocks
     (every head) of the same workload, on this host's cores."""
@@ -258,6 +325,8 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="overwrite 1 GiB between steps (outside the events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the backward pass (bsl_backward) on the same workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 1 GiB device copies (for counter calibration)")
     args = ap.parse_args()
@@ -312,6 +381,7 @@ def main():
         line["library"] = os.environ["BSL_LIBRARY"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(r, log=log)
+    r_w_dtype = r["w"].dtype
     del r
     if args.secondary and args.workload != "c5":
         r5 = time_workload("c5", args.steps, args.warmup, args.cold, log)
@@ -322,6 +392,17 @@ def main():
                              "detail": extra5}
         log(f"[bench] c5: {t5 * 1e3:.3f} ms/step, {roof5['achieved']:.0f} {roof5['unit']} "
             f"({roof5['frac'] * 100:.1f}%)")
+    if args.backward and r_w_dtype == "bf16":
+        rb = time_backward(args.workload, args.steps, args.warmup, log)
+        tb, roofb, extrab = summarize(rb, None)
+        line["backward"] = {"ms_per_step": tb * 1e3, "value": extrab["useful_tflops"],
+                            "unit": "TFLOP/s", "tokens_per_s": extrab["tokens_per_s"],
+                            "roofline": roofb, "detail": extrab}
+        if not args.no_cpu_baseline:
+            line["backward"]["cpu_baseline"] = cpu_baseline_backward(rb, log=log)
+        log(f"[bench] {args.workload} backward: {tb * 1e3:.3f} ms/step, "
+            f"{extrab['useful_tflops']:.1f} useful TFLOP/s ({roofb['frac'] * 100:.1f}% of "
+            f"{roofb['bound']} peak)")
     print(json.dumps(line), flush=True)
 
 

@@ -12,6 +12,11 @@ block pairs    (query block, key block) pairs the kernel computes, each a
 alg. bytes     Q, K, V read once and O written once over the real rows only:
                4 * sum(len) * heads * d * element size.  Halo re-reads, the
                zero rows written for padding and lse are implementation costs.
+
+Backward pass (account_backward): useful FLOP = 10 * d per useful pair (the
+four products dV, dP, dQ, dK, 2d each, plus the scores recomputed once: the
+usual 2.5 times the forward); algorithmic bytes = Q, K, V, O, dO and lse read
+once, dQ, dK, dV written once, over the real rows.
 """
 import numpy as np
 
@@ -59,6 +64,24 @@ def account(lens, heads, d, radius, causal, dtype="bf16"):
     t_mfma = flops / peak
     t_hbm = nbytes / MI355X_HBM_BYTES
     # the bf16 path computes on MFMA; the fp32 path on the vector ALUs
+    compute_unit = "mfma" if dtype == "bf16" else "alu"
+    return dict(useful_pairs=up, block_pairs=bp, tokens=tokens, useful_flops=flops,
+                computed_flops=computed, alg_bytes=nbytes, t_mfma=t_mfma, t_hbm=t_hbm,
+                bound="hbm" if t_hbm >= t_mfma else compute_unit, flops_peak=peak)
+
+
+def account_backward(lens, heads, d, radius, causal, dtype="bf16"):
+    esz = 2 if dtype == "bf16" else 4
+    up = useful_pairs_per_head(lens, radius, causal) * heads
+    bp = block_pairs_per_head(lens, radius, causal) * heads
+    tokens = int(np.sum(lens))
+    flops = 10.0 * d * up
+    # the kernels recompute S and dP in both the dQ and the dK/dV kernel
+    computed = 14.0 * d * BLOCK * BLOCK * bp
+    nbytes = (8.0 * d * esz + 4.0) * tokens * heads
+    peak = MI355X_BF16_DENSE_FLOPS if dtype == "bf16" else MI355X_FP32_VECTOR_FLOPS
+    t_mfma = flops / peak
+    t_hbm = nbytes / MI355X_HBM_BYTES
     compute_unit = "mfma" if dtype == "bf16" else "alu"
     return dict(useful_pairs=up, block_pairs=bp, tokens=tokens, useful_flops=flops,
                 computed_flops=computed, alg_bytes=nbytes, t_mfma=t_mfma, t_hbm=t_hbm,

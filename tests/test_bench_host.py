@@ -126,3 +126,19 @@ def test_summarize_roofline_fields():
     assert extra["tokens_per_s"] == pytest.approx(acc["tokens"] / 1.05e-3)
     assert extra["median_launch_us"] == pytest.approx(1.0e3)
     assert extra["p90_launch_us"] == pytest.approx(1.0e3)
+
+
+def test_account_backward():
+    w = inputs.WORKLOADS["c2"]
+    lens, n = inputs.lengths(w, 42)
+    fwd = workload.account(lens, w.heads, w.d, w.radius, w.causal, w.dtype)
+    bwd = workload.account_backward(lens, w.heads, w.d, w.radius, w.causal, w.dtype)
+    assert bwd["useful_pairs"] == fwd["useful_pairs"]
+    assert bwd["useful_flops"] == 2.5 * fwd["useful_flops"]
+    assert bwd["alg_bytes"] == (8 * w.d * 2 + 4) * int(np.sum(lens)) * w.heads
+    assert bwd["computed_flops"] == 14.0 * w.d * 32 * 32 * fwd["block_pairs"]
+    # the long-context shape is bound by the matrix cores, unlike its forward
+    c4 = inputs.WORKLOADS["c4"]
+    l4, _ = inputs.lengths(c4, 42)
+    b4 = workload.account_backward(l4, c4.heads, c4.d, c4.radius, c4.causal, c4.dtype)
+    assert b4["bound"] == "mfma" and b4["t_mfma"] > b4["t_hbm"]
