@@ -36,7 +36,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-KERNEL_SOURCES = ["block_sparse_local_amd/csrc/fwd_bf16.hip", "block_sparse_local_amd/csrc/launch.h"]
+KERNEL_SOURCES = ["block_sparse_local_amd/csrc/fwd_bf16.hip", "block_sparse_local_amd/csrc/cdna4.h",
+                  "block_sparse_local_amd/csrc/launch.h"]
 
 
 def _scan(src, on_comment, on_space):
