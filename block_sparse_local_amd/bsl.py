@@ -23,8 +23,9 @@ BSL_OK, BSL_E_INVALID, BSL_E_UNSUPPORTED, BSL_E_DEVICE, BSL_E_NOMEM = range(5)
 BSL_BF16, BSL_F32 = 0, 1
 
 # every function include/bsl.h declares
-EXPORTS = ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_backward", "bsl_destroy",
-           "bsl_status_string", "bsl_last_error", "bsl_version")
+EXPORTS = ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_forward_varlen",
+           "bsl_varlen_offsets", "bsl_backward", "bsl_destroy", "bsl_status_string",
+           "bsl_last_error", "bsl_version")
 
 
 class BslError(RuntimeError):
@@ -66,6 +67,9 @@ def load(path=LIB_PATH):
     lib.bsl_create.argtypes = [ctypes.POINTER(BslDesc), ctypes.POINTER(vp)]
     lib.bsl_forward.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.bsl_forward_traced.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.bsl_forward_varlen.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    i32p = ctypes.POINTER(i32)
+    lib.bsl_varlen_offsets.argtypes = [i32, i32p, i32p, i32p, i32p]
     lib.bsl_backward.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.bsl_destroy.argtypes = [vp]
     lib.bsl_status_string.argtypes = [ctypes.c_int]
@@ -74,7 +78,8 @@ def load(path=LIB_PATH):
     lib.bsl_last_error.restype = ctypes.c_char_p
     lib.bsl_version.argtypes = []
     lib.bsl_version.restype = i32
-    for name in ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_backward", "bsl_destroy"):
+    for name in ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_forward_varlen",
+                 "bsl_varlen_offsets", "bsl_backward", "bsl_destroy"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -122,6 +127,26 @@ def bsl_forward_traced(plan, batch, n, q, k, v, o, seqlens, lse, active, masks, 
     _check(load().bsl_forward_traced(plan, batch, n, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                      _ptr(seqlens), _ptr(lse), _ptr(active), _ptr(masks),
                                      _stream(stream)))
+
+
+def bsl_forward_varlen(plan, batch, tokens, max_seqlen, q, k, v, o, cu_seqlens, lse=None,
+                       stream=None):
+    _check(load().bsl_forward_varlen(plan, batch, tokens, max_seqlen, _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(o), _ptr(cu_seqlens), _ptr(lse), _stream(stream)))
+
+
+def bsl_varlen_offsets(lengths):
+    """Host lengths -> (cu_seqlens int32[batch + 1], max_seqlen, ceiling)."""
+    import numpy as np
+    lens = np.ascontiguousarray(lengths, dtype=np.int32)
+    if lens.ndim != 1:
+        raise ValueError("lengths must be one-dimensional")
+    cu = np.zeros(lens.shape[0] + 1, dtype=np.int32)
+    mx, ceil = ctypes.c_int32(), ctypes.c_int32()
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    _check(load().bsl_varlen_offsets(lens.shape[0], lens.ctypes.data_as(i32p),
+                                     cu.ctypes.data_as(i32p), ctypes.byref(mx), ctypes.byref(ceil)))
+    return cu, mx.value, ceil.value
 
 
 def bsl_backward(plan, batch, n, q, k, v, o, dout, lse, seqlens, dq, dk, dv, delta, stream=None):
@@ -204,6 +229,30 @@ class Plan:
         masks = torch.empty((batch, n // 32, w, 32), dtype=torch.int32, device=q.device)
         bsl_forward_traced(self.handle, batch, n, q, k, v, o, seqlens, lse, active, masks, stream)
         return o, active, masks
+
+    def forward_varlen(self, q, k, v, cu_seqlens, max_seqlen, o=None, lse=None, stream=None):
+        """Packed layout: q, k, v [tokens, heads, head_dim]; cu_seqlens int32
+        [batch + 1] on the device; lse float32 [heads, tokens].  See
+        bsl_forward_varlen in include/bsl.h."""
+        import torch
+        tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[self.dtype]
+        if o is None:
+            o = torch.empty_like(q)
+        if q.dim() != 3 or q.shape[1] != self.heads or q.shape[2] != self.head_dim:
+            raise ValueError(f"q must be [tokens, {self.heads}, {self.head_dim}]")
+        for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+            if t.shape != q.shape or t.dtype != tdt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {tdt} CUDA tensor of shape "
+                                 f"{tuple(q.shape)}")
+        if (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1
+                or cu_seqlens.shape[0] < 1):
+            raise ValueError("cu_seqlens must be an int32 CUDA tensor of shape [batch + 1]")
+        if lse is not None and (lse.dtype != torch.float32 or lse.shape != (self.heads, q.shape[0])
+                                or not lse.is_contiguous()):
+            raise ValueError("lse must be a contiguous float32 tensor of shape [heads, tokens]")
+        bsl_forward_varlen(self.handle, cu_seqlens.shape[0] - 1, q.shape[0], max_seqlen, q, k, v,
+                           o, cu_seqlens, lse, stream)
+        return o
 
     def backward(self, q, k, v, o, dout, lse, seqlens=None, dq=None, dk=None, dv=None,
                  delta=None, stream=None):

@@ -86,12 +86,14 @@ bsl_status run(const bsl_plan *plan, int32_t batch, int32_t n, const void *q, co
     a.v = v;
     a.o = o;
     a.seqlens = seqlens;
+    a.cu_seqlens = nullptr;
     a.lse = lse;
     a.active = traced ? active : nullptr;
     a.masks = traced ? masks : nullptr;
     a.batch = batch;
     a.heads = d.heads;
     a.n = n;
+    a.tokens = 0;
     a.head_dim = d.head_dim;
     a.radius = d.radius;
     a.causal = d.causal != 0;
@@ -107,6 +109,68 @@ bool overlaps(const void *a, size_t an, const void *b, size_t bn)
 {
     const uint8_t *x = (const uint8_t *)a, *y = (const uint8_t *)b;
     return x < y + bn && y < x + an;
+}
+
+bsl_status run_varlen(const bsl_plan *plan, int32_t batch, int32_t tokens, int32_t max_seqlen,
+                      const void *q, const void *k, const void *v, void *o,
+                      const int32_t *cu_seqlens, float *lse, void *stream)
+{
+    if (!plan)
+        return fail(BSL_E_INVALID, "plan is NULL");
+    const bsl_desc &d = plan->desc;
+    if (batch < 0 || tokens < 0 || max_seqlen < 0)
+        return fail(BSL_E_INVALID, "batch (%d), tokens (%d) and max_seqlen (%d) must be >= 0",
+                    batch, tokens, max_seqlen);
+    if (batch == 0 || tokens == 0 || max_seqlen == 0)
+        return BSL_OK;
+    if (!cu_seqlens)
+        return fail(BSL_E_INVALID, "cu_seqlens must be a non-NULL device pointer");
+    if (!q || !k || !v || !o)
+        return fail(BSL_E_INVALID, "q, k, v and o must be non-NULL device pointers");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(BSL_E_INVALID, "q, k, v and o must be 16-byte aligned");
+    const long double elems = (long double)tokens * d.heads * (long double)d.head_dim;
+    if (elems > 9.0e18L)
+        return fail(BSL_E_INVALID, "tensor of %d x %d x %d elements is too large", tokens,
+                    d.heads, d.head_dim);
+    const long long nblk = ((long long)max_seqlen + d.block_size - 1) / d.block_size;
+    if ((long long)batch * d.heads * nblk > 0x7fffffffLL)
+        return fail(BSL_E_INVALID, "batch * heads * ceil(max_seqlen / 32) exceeds 2^31 - 1");
+    const size_t esz = d.dtype == BSL_BF16 ? 2 : 4;
+    const size_t bytes = (size_t)elems * esz;
+    for (const void *in : {q, k, v})
+        if (overlaps(o, bytes, in, bytes))
+            return fail(BSL_E_INVALID, "o overlaps one of q, k, v");
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return fail(BSL_E_DEVICE, "hipGetDevice failed");
+    if (dev != plan->device)
+        return fail(BSL_E_INVALID, "current device %d is not the plan's device %d", dev,
+                    plan->device);
+
+    bsl::Launch a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.seqlens = nullptr;
+    a.cu_seqlens = cu_seqlens;
+    a.lse = lse;
+    a.active = nullptr;
+    a.masks = nullptr;
+    a.batch = batch;
+    a.heads = d.heads;
+    a.n = max_seqlen;
+    a.tokens = tokens;
+    a.head_dim = d.head_dim;
+    a.radius = d.radius;
+    a.causal = d.causal != 0;
+    a.scale = plan->scale;
+    a.stream = (hipStream_t)stream;
+    const hipError_t e = d.dtype == BSL_BF16 ? bsl::launch_fwd_bf16(a) : bsl::launch_fwd_f32(a);
+    if (e != hipSuccess)
+        return fail(BSL_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    return BSL_OK;
 }
 
 bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
@@ -264,6 +328,41 @@ bsl_status bsl_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
                         float *delta, void *stream)
 {
     return run_backward(plan, batch, n, q, k, v, o, dout, lse, seqlens, dq, dk, dv, delta, stream);
+}
+
+bsl_status bsl_forward_varlen(const bsl_plan *plan, int32_t batch, int32_t tokens,
+                              int32_t max_seqlen, const void *q, const void *k, const void *v,
+                              void *o, const int32_t *cu_seqlens, float *lse, void *stream)
+{
+    return run_varlen(plan, batch, tokens, max_seqlen, q, k, v, o, cu_seqlens, lse, stream);
+}
+
+bsl_status bsl_varlen_offsets(int32_t batch, const int32_t *lengths, int32_t *cu_seqlens,
+                              int32_t *max_seqlen, int32_t *ceiling)
+{
+    if (batch < 0)
+        return fail(BSL_E_INVALID, "batch must be >= 0 (got %d)", batch);
+    if (!cu_seqlens || !max_seqlen || !ceiling || (batch > 0 && !lengths))
+        return fail(BSL_E_INVALID, "lengths, cu_seqlens, max_seqlen and ceiling must be non-NULL");
+    long long sum = 0;
+    int32_t mx = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        if (lengths[b] < 0)
+            return fail(BSL_E_INVALID, "lengths[%d] = %d is negative", b, lengths[b]);
+        sum += lengths[b];
+        if (sum > 0x7fffffffLL)
+            return fail(BSL_E_INVALID, "the lengths sum past 2^31 - 1");
+        mx = lengths[b] > mx ? lengths[b] : mx;
+    }
+    const long long ceil32 = ((long long)mx + 31) / 32 * 32;
+    if (ceil32 > 0x7fffffffLL)
+        return fail(BSL_E_INVALID, "the longest length rounds up past 2^31 - 1");
+    cu_seqlens[0] = 0;
+    for (int32_t b = 0; b < batch; ++b)
+        cu_seqlens[b + 1] = cu_seqlens[b] + lengths[b];
+    *max_seqlen = mx;
+    *ceiling = (int32_t)ceil32;
+    return BSL_OK;
 }
 
 bsl_status bsl_destroy(bsl_plan *plan)

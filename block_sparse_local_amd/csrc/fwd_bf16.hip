@@ -80,12 +80,42 @@ constexpr float RESCALE_SLACK = BSL_RESCALE_SLACK; // in log2 units
 struct Params {
     const uint16_t *q, *k, *v;
     uint16_t *o;
-    const int32_t *seqlens;
+    const int32_t *seqlens; // padded layout: lengths (or nullptr)
+    const int32_t *cu;      // packed layout: sequence start offsets, batch + 1 of them
     float *lse;
     int32_t *active;
     uint32_t *masks;
+    // n: padded buffer length, or the longest sequence the grid covers (packed)
     int32_t heads, n, nblk, ngroups, radius, total;
-    float c; // scale * log2(e)
+    int32_t tokens; // packed layout: rows in the buffer
+    float c;        // scale * log2(e)
+};
+
+// Where sequence b's rows of head h live, and how many are real.  Padded layout
+// [batch][heads][n][D]: rows D apart from (b heads + h) n D.  Packed layout
+// [tokens][heads][D]: rows heads D apart from (cu[b] heads + h) D, lse
+// [heads][tokens].  Offsets read from the device are clamped so that every row
+// index below stays inside the buffer whatever they hold.
+template <int D, bool VARLEN>
+struct Seq {
+    size_t base, lse_base;
+    int len;
+    __device__ __forceinline__ Seq(const Params &p, int b, int h, int bh)
+    {
+        if (VARLEN) {
+            int s0 = p.cu[b], s1 = p.cu[b + 1];
+            s0 = s0 < 0 ? 0 : (s0 > p.tokens ? p.tokens : s0);
+            s1 = s1 < s0 ? s0 : (s1 > p.tokens ? p.tokens : s1);
+            len = s1 - s0 > p.n ? p.n : s1 - s0;
+            base = ((size_t)s0 * (size_t)p.heads + (size_t)h) * D;
+            lse_base = (size_t)h * (size_t)p.tokens + (size_t)s0;
+        } else {
+            len = p.seqlens ? p.seqlens[b] : p.n;
+            len = len < 0 ? 0 : (len > p.n ? p.n : len);
+            base = (size_t)bh * (size_t)p.n * D;
+            lse_base = (size_t)bh * (size_t)p.n;
+        }
+    }
 };
 
 // Workgroup order: each XCD's contiguous run of query groups (see
@@ -113,10 +143,13 @@ struct Tile {
     }
 };
 
-template <int D, int MQ, int NSTAGE, bool CAUSAL, bool TRACE>
+template <int D, int MQ, int NSTAGE, bool CAUSAL, bool TRACE, bool VARLEN>
 __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
 {
     using T = Tile<D>;
+    static_assert(!(TRACE && VARLEN), "the trace describes the padded layout");
+    // distance between consecutive rows of one head, in elements
+    const size_t RS = VARLEN ? (size_t)p.heads * D : (size_t)D;
     constexpr int NT = MQ * 64;
     constexpr int NMT = D / 32;                 // 32-wide output tiles
     constexpr int NKS = D / 16;                 // 16-deep steps of the score contraction
@@ -140,16 +173,19 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
     const int grp = g % p.ngroups;
     const int bh = g / p.ngroups;
     const int b = bh / p.heads, h = bh % p.heads;
-    int len = p.seqlens ? p.seqlens[b] : p.n;
-    len = len < 0 ? 0 : (len > p.n ? p.n : len);
+    const Seq<D, VARLEN> sq(p, b, h, bh);
+    const int len = sq.len;
     const int nb = (len + BLK - 1) / BLK;
     const int R = p.radius, W = 2 * R + 1;
     const int i0 = grp * MQ;
     const int i = i0 + wave;
-    const bool exists = i < p.nblk;
+    // packed layout: rows past the sequence belong to the next one, so only the
+    // sequence's own blocks exist; padded layout: every block of the buffer does
+    // (blocks of padding get zero rows)
+    const bool exists = i < (VARLEN ? nb : p.nblk);
     const bool trace_here = TRACE && h == 0;
 
-    const size_t base = (size_t)bh * (size_t)p.n * D;
+    const size_t base = sq.base;
     const uint16_t *qg = p.q + base;
     const uint16_t *kg = p.k + base;
     const uint16_t *vg = p.v + base;
@@ -158,12 +194,12 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
 
     // ------------------------------------------------ blocks of pure padding
     if (i0 >= nb) {
-        if (exists) {
+        if (!VARLEN && exists) {
             uint16_t *ob = og + (size_t)i * BLK * D;
             for (int c = lane; c < BLK * D / 8; c += 64)
                 *(u32x4 *)(ob + (size_t)c * 8) = u32x4{0, 0, 0, 0};
             if (p.lse && half == 0)
-                p.lse[(size_t)bh * p.n + (size_t)i * BLK + col] = -INFINITY;
+                p.lse[sq.lse_base + (size_t)i * BLK + col] = -INFINITY;
             if (trace_here) {
                 for (int s = lane; s < W; s += 64)
                     p.active[trace_row + s] = -1;
@@ -215,7 +251,10 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
             const int t = is_v ? s - SLOTS / 2 : s;
             const int r = t / T::CPR, cp = t % T::CPR;
             const int c = cp ^ (is_v ? T::v_swz(r) : T::k_swz(r));
-            const uint16_t *src = (is_v ? vg : kg) + (size_t)(j * BLK + r) * D + c * 8;
+            // packed layout: rows past the end repeat the last row (in bounds;
+            // masked below); the padded buffer holds all 32 rows
+            const int row = VARLEN ? min(j * BLK + r, len - 1) : j * BLK + r;
+            const uint16_t *src = (is_v ? vg : kg) + (size_t)row * RS + c * 8;
             uint8_t *dst = lds + stage * STAGE + (u * NT + wave * 64) * 16;
             __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
         }
@@ -229,7 +268,7 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
     for (int s = 0; s < NKS; ++s) {
         u32x4 x = u32x4{0, 0, 0, 0};
         if (qvalid)
-            x = *(const u32x4 *)(qg + (size_t)qrow * D + s * 16 + half * 8);
+            x = *(const u32x4 *)(qg + (size_t)qrow * RS + s * 16 + half * 8);
         qf[s] = as_bf16x8(x);
     }
 
@@ -379,8 +418,11 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
     const float lt = lsum + __shfl_xor(lsum, 32);
     if (!exists)
         return;
+    // packed layout: a row past the sequence's end is the next sequence's
+    if (VARLEN && !qvalid)
+        return;
     const float inv = qvalid ? 1.0f / lt : 0.0f;
-    uint16_t *orow = og + (size_t)qrow * D;
+    uint16_t *orow = og + (size_t)qrow * RS;
 #pragma unroll
     for (int m = 0; m < NMT; ++m) {
 #pragma unroll
@@ -397,7 +439,7 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
         }
     }
     if (p.lse && half == 0)
-        p.lse[(size_t)bh * p.n + (size_t)qrow] =
+        p.lse[sq.lse_base + (size_t)qrow] =
             qvalid ? (m_used + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
     if (trace_here) {
         const int used = hi_w >= lo_w ? hi_w - lo_w + 1 : 0;
@@ -409,10 +451,10 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
     }
 }
 
-template <int D, int MQ, int NSTAGE, bool CAUSAL, bool TRACE>
+template <int D, int MQ, int NSTAGE, bool CAUSAL, bool TRACE, bool VARLEN>
 hipError_t launch_t(const Launch &a, const Params &p)
 {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, MQ, NSTAGE, CAUSAL, TRACE>), dim3(p.total),
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MQ, NSTAGE, CAUSAL, TRACE, VARLEN>), dim3(p.total),
                        dim3(MQ * 64), 0, a.stream, p);
     return hipGetLastError();
 }
@@ -420,12 +462,15 @@ hipError_t launch_t(const Launch &a, const Params &p)
 template <int D, int MQ, int NSTAGE>
 hipError_t launch_d(const Launch &a, const Params &p)
 {
+    if (a.cu_seqlens)
+        return a.causal ? launch_t<D, MQ, NSTAGE, true, false, true>(a, p)
+                        : launch_t<D, MQ, NSTAGE, false, false, true>(a, p);
     const bool tr = a.active != nullptr;
     if (a.causal)
-        return tr ? launch_t<D, MQ, NSTAGE, true, true>(a, p)
-                  : launch_t<D, MQ, NSTAGE, true, false>(a, p);
-    return tr ? launch_t<D, MQ, NSTAGE, false, true>(a, p)
-              : launch_t<D, MQ, NSTAGE, false, false>(a, p);
+        return tr ? launch_t<D, MQ, NSTAGE, true, true, false>(a, p)
+                  : launch_t<D, MQ, NSTAGE, true, false, false>(a, p);
+    return tr ? launch_t<D, MQ, NSTAGE, false, true, false>(a, p)
+              : launch_t<D, MQ, NSTAGE, false, false, false>(a, p);
 }
 
 } // namespace
@@ -457,12 +502,14 @@ hipError_t launch_fwd_bf16(const Launch &a)
     p.v = (const uint16_t *)a.v;
     p.o = (uint16_t *)a.o;
     p.seqlens = a.seqlens;
+    p.cu = a.cu_seqlens;
     p.lse = a.lse;
     p.active = a.active;
     p.masks = a.masks;
     p.heads = a.heads;
     p.n = a.n;
-    p.nblk = a.n / BLK;
+    p.tokens = a.tokens;
+    p.nblk = (a.n + BLK - 1) / BLK;
     p.ngroups = (p.nblk + MQ - 1) / MQ;
     p.radius = a.radius;
     p.total = a.batch * a.heads * p.ngroups;

@@ -26,18 +26,26 @@ constexpr float LN2 = 0.6931471805599453f;
 struct Params {
     const float *q, *k, *v;
     float *o;
-    const int32_t *seqlens;
+    const int32_t *seqlens; // padded layout: lengths (or nullptr)
+    const int32_t *cu;      // packed layout: sequence start offsets, batch + 1 of them
     float *lse;
     int32_t *active;
     uint32_t *masks;
+    // n: padded buffer length, or the longest sequence the grid covers (packed)
     int32_t heads, n, nblk, radius, total;
-    float c; // scale * log2(e)
+    int32_t tokens; // packed layout: rows in the buffer
+    float c;        // scale * log2(e)
 };
 
-template <int D, bool CAUSAL, bool TRACE>
+// Padded layout [batch][heads][n][D]: rows D apart.  Packed layout
+// [tokens][heads][D]: sequence b's rows of head h start at (cu[b] heads + h) D,
+// heads D apart, lse [heads][tokens]; offsets are clamped into the buffer.
+template <int D, bool CAUSAL, bool TRACE, bool VARLEN>
 __global__ void __launch_bounds__(256) fwd_f32_kernel(Params p)
 {
+    static_assert(!(TRACE && VARLEN), "the trace describes the padded layout");
     constexpr int E = D / 8; // dims per thread
+    const size_t RS = VARLEN ? (size_t)p.heads * D : (size_t)D;
     __shared__ float kl[BLK][D + 1];
     __shared__ float vl[BLK][D + 1];
 
@@ -47,11 +55,26 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(Params p)
     const int i = g % p.nblk;
     const int bh = g / p.nblk;
     const int b = bh / p.heads, h = bh % p.heads;
-    int len = p.seqlens ? p.seqlens[b] : p.n;
-    len = len < 0 ? 0 : (len > p.n ? p.n : len);
+    int len;
+    size_t base, lse_base;
+    if (VARLEN) {
+        int s0 = p.cu[b], s1 = p.cu[b + 1];
+        s0 = s0 < 0 ? 0 : (s0 > p.tokens ? p.tokens : s0);
+        s1 = s1 < s0 ? s0 : (s1 > p.tokens ? p.tokens : s1);
+        len = s1 - s0 > p.n ? p.n : s1 - s0;
+        base = ((size_t)s0 * (size_t)p.heads + (size_t)h) * D;
+        lse_base = (size_t)h * (size_t)p.tokens + (size_t)s0;
+    } else {
+        len = p.seqlens ? p.seqlens[b] : p.n;
+        len = len < 0 ? 0 : (len > p.n ? p.n : len);
+        base = (size_t)bh * (size_t)p.n * D;
+        lse_base = (size_t)bh * (size_t)p.n;
+    }
     const int nb = (len + BLK - 1) / BLK;
+    // packed layout: blocks past the sequence hold the next sequence's rows
+    if (VARLEN && i >= nb)
+        return;
     const int R = p.radius, W = 2 * R + 1;
-    const size_t base = (size_t)bh * (size_t)p.n * D;
     const int t = i * BLK + r;
     const bool tvalid = t < len;
     const bool trace_here = TRACE && h == 0;
@@ -68,7 +91,7 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(Params p)
     float qv[E], ov[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        qv[e] = tvalid ? p.q[base + (size_t)t * D + e * 8 + sub] : 0.0f;
+        qv[e] = tvalid ? p.q[base + (size_t)t * RS + e * 8 + sub] : 0.0f;
         ov[e] = 0.0f;
     }
     float m = -INFINITY, l = 0.0f;
@@ -78,8 +101,10 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(Params p)
         for (int x = tid; x < BLK * D; x += 256) {
             const int kr = x / D, kc = x % D;
             const int s = j * BLK + kr;
-            kl[kr][kc] = p.k[base + (size_t)s * D + kc];
-            const float vv = p.v[base + (size_t)s * D + kc];
+            // packed layout: rows past the end repeat the last row (masked)
+            const int sr = VARLEN ? min(s, len - 1) : s;
+            kl[kr][kc] = p.k[base + (size_t)sr * RS + kc];
+            const float vv = p.v[base + (size_t)sr * RS + kc];
             vl[kr][kc] = s < len ? vv : 0.0f; // padded keys: zero V, never NaN
         }
         __syncthreads();
@@ -127,12 +152,14 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(Params p)
         m = mn;
     }
 
+    if (VARLEN && !tvalid)
+        return; // the next sequence's row
     const float inv = tvalid ? 1.0f / l : 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e)
-        p.o[base + (size_t)t * D + e * 8 + sub] = tvalid ? ov[e] * inv : 0.0f;
+        p.o[base + (size_t)t * RS + e * 8 + sub] = tvalid ? ov[e] * inv : 0.0f;
     if (p.lse && sub == 0)
-        p.lse[(size_t)bh * p.n + (size_t)t] =
+        p.lse[lse_base + (size_t)t] =
             tvalid ? (m + __builtin_amdgcn_logf(l)) * LN2 : -INFINITY;
     if (trace_here) {
         const int used = hi >= lo ? hi - lo + 1 : 0;
@@ -144,20 +171,23 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(Params p)
     }
 }
 
-template <int D, bool CAUSAL, bool TRACE>
+template <int D, bool CAUSAL, bool TRACE, bool VARLEN>
 hipError_t launch_t(const Launch &a, const Params &p)
 {
-    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, TRACE>), dim3(p.total), dim3(256), 0, a.stream, p);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, TRACE, VARLEN>), dim3(p.total), dim3(256), 0,
+                       a.stream, p);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const Launch &a, const Params &p)
 {
+    if (a.cu_seqlens)
+        return a.causal ? launch_t<D, true, false, true>(a, p) : launch_t<D, false, false, true>(a, p);
     const bool tr = a.active != nullptr;
     if (a.causal)
-        return tr ? launch_t<D, true, true>(a, p) : launch_t<D, true, false>(a, p);
-    return tr ? launch_t<D, false, true>(a, p) : launch_t<D, false, false>(a, p);
+        return tr ? launch_t<D, true, true, false>(a, p) : launch_t<D, true, false, false>(a, p);
+    return tr ? launch_t<D, false, true, false>(a, p) : launch_t<D, false, false, false>(a, p);
 }
 
 } // namespace
@@ -170,12 +200,14 @@ hipError_t launch_fwd_f32(const Launch &a)
     p.v = (const float *)a.v;
     p.o = (float *)a.o;
     p.seqlens = a.seqlens;
+    p.cu = a.cu_seqlens;
     p.lse = a.lse;
     p.active = a.active;
     p.masks = a.masks;
     p.heads = a.heads;
     p.n = a.n;
-    p.nblk = a.n / BLK;
+    p.tokens = a.tokens;
+    p.nblk = (a.n + BLK - 1) / BLK;
     p.radius = a.radius;
     p.total = a.batch * a.heads * p.nblk;
     p.c = a.scale * LOG2E;

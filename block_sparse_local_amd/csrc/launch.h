@@ -6,15 +6,19 @@
 
 namespace bsl {
 
-// One forward call, after argument validation.
+// One forward call, after argument validation.  Padded layout: cu_seqlens is
+// nullptr and n is the buffer length.  Packed layout: cu_seqlens is set, n is
+// the longest sequence the grid must cover and tokens the rows in the buffer.
 struct Launch {
     const void *q, *k, *v;
     void *o;
-    const int32_t *seqlens; // device; nullptr = every sequence is n long
-    float *lse;             // device or nullptr
-    int32_t *active;        // trace outputs (nullptr unless traced)
+    const int32_t *seqlens;    // device; nullptr = every sequence is n long
+    const int32_t *cu_seqlens; // device, batch + 1 offsets (packed layout only)
+    float *lse;                // device or nullptr
+    int32_t *active;           // trace outputs (nullptr unless traced)
     uint32_t *masks;
     int32_t batch, heads, n, head_dim, radius;
+    int32_t tokens;
     bool causal;
     float scale; // already resolved (> 0)
     hipStream_t stream;

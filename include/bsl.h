@@ -20,14 +20,16 @@
  * created on.  n is the padded buffer length (a multiple of 32).  Row t of a
  * sequence with length L is real when t < L; rows t >= L are padding: their
  * Q/K/V values are never used (they may hold NaN) and their O rows are written
- * as zeros.
+ * as zeros.  bsl_forward_varlen takes the packed alternative: the sequences
+ * back to back in [tokens][heads][head_dim] arrays, located by offsets.
  *
  * Ownership.  The caller owns every buffer.  A plan holds only immutable
  * settings and device facts; it allocates no device memory, so one plan may be
  * used from several host threads and streams at once.
  *
- * Asynchrony.  bsl_forward and bsl_forward_traced only enqueue work on the
- * given stream (NULL = the default stream) and never synchronise.
+ * Asynchrony.  bsl_forward, bsl_forward_traced, bsl_forward_varlen and
+ * bsl_backward only enqueue work on the given stream (NULL = the default
+ * stream) and never synchronise.
  *
  * Errors.  Every call returns a bsl_status.  Argument errors are reported
  * before anything is launched, and then nothing is written.  A failed launch
@@ -43,7 +45,7 @@
 extern "C" {
 #endif
 
-#define BSL_VERSION 10100 /* major * 10000 + minor * 100 + patch */
+#define BSL_VERSION 10200 /* major * 10000 + minor * 100 + patch */
 
 typedef enum bsl_status {
     BSL_OK = 0,
@@ -109,6 +111,56 @@ bsl_status bsl_forward(const bsl_plan *plan, int32_t batch, int32_t n, const voi
 bsl_status bsl_forward_traced(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
                               const void *k, const void *v, void *o, const int32_t *seqlens,
                               float *lse, int32_t *active, uint32_t *masks, void *stream);
+
+/* bsl_forward over a packed batch: the sequences lie back to back with no
+ * padding between them (the padding the page's section 1, "Padding Waste",
+ * counts as wasted memory and bandwidth), addressed by offsets.  The operation
+ * per sequence is exactly bsl_forward's on that sequence alone: same band, same
+ * masks, same arithmetic, so each row's output equals bit for bit the one
+ * bsl_forward writes for the same data in the padded layout.
+ *   batch       >= 0 sequences.
+ *   tokens      >= 0 rows in the packed buffers (the sum of the lengths).
+ *   max_seqlen  >= 0, a bound on every length; it sizes the launch, so the host
+ *               need not read cu_seqlens.  A sequence longer than max_seqlen is
+ *               treated as its first max_seqlen rows; the rest of its rows are
+ *               not written.
+ *   q, k, v     device pointers, [tokens][heads][head_dim] in the plan's dtype:
+ *               row t of sequence b, head h, is at ((cu_seqlens[b] + t) * heads
+ *               + h) * head_dim.  This is the projection's own output layout,
+ *               with no transpose.
+ *   o           device pointer, same shape and dtype; only the rows of the
+ *               sequences are written: rows outside every [cu_seqlens[b],
+ *               cu_seqlens[b+1]) are left as they were.  It must not overlap
+ *               q, k or v.
+ *   cu_seqlens  device int32[batch + 1], non-decreasing, cu_seqlens[0] = 0,
+ *               cu_seqlens[batch] <= tokens: sequence b is rows [cu_seqlens[b],
+ *               cu_seqlens[b+1]).  Values are clamped into [0, tokens] on the
+ *               device (a decreasing pair gives an empty sequence), so no
+ *               value can send an access outside the buffers.  Out-of-order
+ *               offsets make later sequences overlap earlier ones; rows two
+ *               sequences share get either's value.
+ *   lse         device float[heads][tokens] or NULL: as in bsl_forward, for the
+ *               sequences' rows.
+ *   stream      a hipStream_t, or NULL for the default stream.
+ * batch, tokens or max_seqlen == 0 is a no-op returning BSL_OK.  Returns
+ * BSL_E_INVALID for a NULL plan or cu_seqlens, negative sizes, a NULL or
+ * misaligned (not 16-byte) q/k/v/o, o overlapping an input, sizes past the
+ * limits of bsl_forward, or a current device that is not the plan's. */
+bsl_status bsl_forward_varlen(const bsl_plan *plan, int32_t batch, int32_t tokens,
+                              int32_t max_seqlen, const void *q, const void *k, const void *v,
+                              void *o, const int32_t *cu_seqlens, float *lse, void *stream);
+
+/* Host-side collation of a batch's lengths (section 2, item 2 of the page,
+ * "Dynamic Ceiling Hardware Alignment"): from host int32 lengths[batch] (each
+ * >= 0) write host int32 cu_seqlens[batch + 1] (exclusive prefix sums, the
+ * offsets bsl_forward_varlen takes), *max_seqlen (the longest length) and
+ * *ceiling (that length rounded up to the next multiple of 32: the buffer
+ * length n a padded batch needs for bsl_forward).  No device work.
+ * BSL_E_INVALID for batch < 0, a NULL pointer (lengths may be NULL when batch
+ * is 0), a negative length, or a sum or ceiling past 2^31 - 1; nothing is
+ * written then. */
+bsl_status bsl_varlen_offsets(int32_t batch, const int32_t *lengths, int32_t *cu_seqlens,
+                              int32_t *max_seqlen, int32_t *ceiling);
 
 /* Enqueue the backward pass of bsl_forward (NucleoByte project page, section 3,
  * "Custom Backpropagation"): from the output gradient dO, the gradients dQ, dK,

@@ -6,9 +6,10 @@ import re
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
-from block_sparse_local_amd import bsl
+from block_sparse_local_amd import bsl, inputs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bsl.h")
@@ -81,7 +82,53 @@ def test_null_arguments(lib):
     assert "plan" in bsl.bsl_last_error()
     assert lib.bsl_forward_traced(None, 1, 32, 16, 16, 16, 16, None, None, 16, 16,
                                   None) == bsl.BSL_E_INVALID
+    assert lib.bsl_forward_varlen(None, 1, 64, 64, 16, 16, 16, 16, 16, None,
+                                  None) == bsl.BSL_E_INVALID
+    assert "plan" in bsl.bsl_last_error()
     assert lib.bsl_destroy(None) == bsl.BSL_OK
+
+
+def test_varlen_offsets_collate_lengths(lib):
+    """The host collator: exclusive prefix sums, the longest length and the
+    dynamic ceiling (the longest length rounded up to a multiple of 32)."""
+    rng = np.random.default_rng(4)
+    for lens in ([], [0], [1], [32], [33, 0, 5], list(rng.integers(0, 3000, 64))):
+        cu, mx, ceil = bsl.bsl_varlen_offsets(lens)
+        assert cu.tolist() == [0] + np.cumsum(np.asarray(lens, np.int64)).tolist()
+        assert mx == (max(lens) if len(lens) else 0)
+        assert ceil % 32 == 0 and ceil - 32 < mx <= ceil if mx else ceil == 0
+    # the ragged mRNA batch: the ceiling is the padded buffer length it is drawn with
+    w = inputs.WORKLOADS["c2"]
+    lens, n = inputs.lengths(w, 42)
+    cu, mx, ceil = bsl.bsl_varlen_offsets(lens)
+    assert ceil == n and mx == int(lens.max()) and cu[-1] == int(lens.sum())
+
+
+@pytest.mark.parametrize("lens", [[3, -1, 4], [2 ** 31 - 1, 1], [2 ** 31 - 20]])
+def test_varlen_offsets_reject_bad_lengths_and_write_nothing(lib, lens):
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    a = np.asarray(lens, np.int32)
+    cu = np.full(len(lens) + 1, -7, np.int32)
+    mx, ceil = ctypes.c_int32(-7), ctypes.c_int32(-7)
+    st = lib.bsl_varlen_offsets(len(lens), a.ctypes.data_as(i32p), cu.ctypes.data_as(i32p),
+                                ctypes.byref(mx), ctypes.byref(ceil))
+    assert st == bsl.BSL_E_INVALID and bsl.bsl_last_error() != ""
+    assert np.all(cu == -7) and mx.value == -7 and ceil.value == -7
+
+
+def test_varlen_offsets_null_pointers(lib):
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    cu = np.zeros(2, np.int32)
+    a = np.ones(1, np.int32)
+    mx, ceil = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.bsl_varlen_offsets(1, None, cu.ctypes.data_as(i32p), ctypes.byref(mx),
+                                  ctypes.byref(ceil)) == bsl.BSL_E_INVALID
+    assert lib.bsl_varlen_offsets(1, a.ctypes.data_as(i32p), None, ctypes.byref(mx),
+                                  ctypes.byref(ceil)) == bsl.BSL_E_INVALID
+    assert lib.bsl_varlen_offsets(-1, a.ctypes.data_as(i32p), cu.ctypes.data_as(i32p),
+                                  ctypes.byref(mx), ctypes.byref(ceil)) == bsl.BSL_E_INVALID
+    assert lib.bsl_varlen_offsets(0, None, cu.ctypes.data_as(i32p), ctypes.byref(mx),
+                                  ctypes.byref(ceil)) == bsl.BSL_OK
 
 
 def test_binding_raises_on_error(lib):
