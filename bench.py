@@ -114,7 +114,17 @@ def to_device(x, dtype):
     return torch.from_numpy(x).cuda()
 
 
-def time_workload(key, steps, warmup, cold=False, log=print):
+def pack_device(x, lens):
+    """[batch, heads, n, d] device tensor -> the packed [tokens, heads, d] layout
+    (each sequence's real rows, token-major, back to back)."""
+    import torch
+    return torch.cat([x[b, :, :int(L)].transpose(0, 1) for b, L in enumerate(lens)]).contiguous()
+
+
+def time_workload(key, steps, warmup, cold=False, log=print, layout="padded"):
+    """Times bsl_forward on the workload (layout "padded": [batch][heads][n][d])
+    or bsl_forward_varlen on the same sequences packed ("packed":
+    [tokens][heads][d], no padding between sequences)."""
     import torch
     from block_sparse_local_amd import bsl, inputs, workload
 
@@ -122,17 +132,29 @@ def time_workload(key, steps, warmup, cold=False, log=print):
     d = inputs.make(key, 42)
     w = d["workload"]
     lens = d["seqlens"]
-    log(f"[bench] {key} inputs drawn in {time.time() - t0:.1f}s: {w.describe()}")
+    log(f"[bench] {key} inputs drawn in {time.time() - t0:.1f}s: {w.describe()} ({layout})")
     q, k, v = (to_device(d[x], w.dtype) for x in ("q", "k", "v"))
-    o = torch.empty_like(q)
-    sl = torch.from_numpy(lens).cuda()
     plan = bsl.Plan(w.d, w.heads, w.radius, w.causal, w.dtype)
+    if layout == "packed":
+        q, k, v = (pack_device(x, lens) for x in (q, k, v))
+        cu_host, max_len, _ = bsl.bsl_varlen_offsets(lens)
+        cu = torch.from_numpy(cu_host).cuda()
+
+        def call():
+            plan.forward_varlen(q, k, v, cu, max_len, o=o, stream=stream)
+    else:
+        sl = torch.from_numpy(lens).cuda()
+
+        def call():
+            plan.forward(q, k, v, sl, o=o, stream=stream)
+    o = torch.empty_like(q)
+    buffer_bytes = 4 * q.numel() * q.element_size()
     acc = workload.account(lens, w.heads, w.d, w.radius, w.causal, w.dtype)
     stream = torch.cuda.current_stream()
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if cold else None
 
     for _ in range(warmup):
-        plan.forward(q, k, v, sl, o=o, stream=stream)
+        call()
     torch.cuda.synchronize()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -143,7 +165,7 @@ def time_workload(key, steps, warmup, cold=False, log=print):
         if flush is not None:
             flush.fill_(float(s))
         starts[s].record(stream)
-        plan.forward(q, k, v, sl, o=o, stream=stream)
+        call()
         ends[s].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_begin
@@ -151,7 +173,8 @@ def time_workload(key, steps, warmup, cold=False, log=print):
     plan.close()
     del q, k, v, o, flush
     torch.cuda.empty_cache()
-    return dict(key=key, w=w, d=d, acc=acc, wall=wall, per_launch=per_launch, steps=steps)
+    return dict(key=key, w=w, d=d, acc=acc, wall=wall, per_launch=per_launch, steps=steps,
+                layout=layout, buffer_bytes=buffer_bytes)
 
 
 def time_backward(key, steps, warmup, log=print):
@@ -328,6 +351,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward pass (bsl_backward) on the same workload")
+    ap.add_argument("--varlen", action="store_true",
+                    help="also time the same workload in the packed layout (bsl_forward_varlen)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 1 GiB device copies (for counter calibration)")
     args = ap.parse_args()
@@ -383,7 +408,22 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(r, log=log)
     r_w_dtype = r["w"].dtype
+    padded_bytes = r["buffer_bytes"]
     del r
+    if args.varlen:
+        rv = time_workload(args.workload, args.steps, args.warmup, args.cold, log, "packed")
+        tv, roofv, extrav = summarize(rv, None)
+        line["varlen"] = {"layout": "packed [tokens][heads][head_dim], offsets cu_seqlens",
+                          "ms_per_step": tv * 1e3, "value": extrav["useful_tflops"],
+                          "unit": "TFLOP/s", "tokens_per_s": extrav["tokens_per_s"],
+                          "roofline": roofv, "detail": extrav,
+                          "buffer_bytes": rv["buffer_bytes"],
+                          "padded_buffer_bytes": padded_bytes,
+                          "padded_ms_per_step": t_step * 1e3}
+        log(f"[bench] {args.workload} packed: {tv * 1e3:.3f} ms/step "
+            f"({roofv['frac'] * 100:.1f}% of {roofv['bound']} peak); buffers "
+            f"{rv['buffer_bytes'] / 2**20:.1f} MiB vs {padded_bytes / 2**20:.1f} MiB padded")
+        del rv
     if args.secondary and args.workload != "c5":
         r5 = time_workload("c5", args.steps, args.warmup, args.cold, log)
         t5, roof5, extra5 = summarize(r5, stored_traffic("c5"))

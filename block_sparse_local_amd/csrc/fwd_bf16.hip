@@ -170,9 +170,14 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
     const int col = lane & 31, half = lane >> 5;
 
     const int g = xcd_remap((int)blockIdx.x, p.total);
-    const int grp = g % p.ngroups;
-    const int bh = g / p.ngroups;
-    const int b = bh / p.heads, h = bh % p.heads;
+    // Padded layout: a head's query groups are consecutive, so a run of groups
+    // streams through one contiguous [n][D] slice.  Packed layout: a token's
+    // heads sit side by side in memory, so the heads of one query group are
+    // consecutive and a run of groups reads whole token rows.
+    const int grp = VARLEN ? (g / p.heads) % p.ngroups : g % p.ngroups;
+    const int b = VARLEN ? g / p.heads / p.ngroups : g / p.ngroups / p.heads;
+    const int h = VARLEN ? g % p.heads : (g / p.ngroups) % p.heads;
+    const int bh = b * p.heads + h;
     const Seq<D, VARLEN> sq(p, b, h, bh);
     const int len = sq.len;
     const int nb = (len + BLK - 1) / BLK;
