@@ -137,3 +137,66 @@ def make(key: str, seed: int = 42, poison: bool = False, heads=None, n=None, gra
     if grad:
         out["dout"] = t[3]
     return out
+
+
+# ------------------------------------------------------------ nucleotide text
+# Stand-in for the transcript corpus the NucleoByte page trains on (GENCODE
+# transcripts, FASTA): ASCII bases back to back with byte offsets per sequence.
+# Draws only: bases uniform over A, C, G, T; about one base in a thousand an
+# 'N' (an unknown base, as FASTA files carry); runs of soft-masked (lowercase)
+# bases covering about a tenth of the text.  One PCG64 stream per slab,
+# ``default_rng([seed, cfg, 6])``; lengths from ``default_rng([seed, cfg, 3])``.
+
+@dataclass(frozen=True)
+class DnaWorkload:
+    key: str
+    cfg: int
+    name: str
+    batch: int
+    lo: int          # shortest sequence, bases
+    hi: int          # longest sequence, bases
+    k: int = 6
+
+    def describe(self):
+        return (f"{self.name}: {self.batch} sequences of {self.lo}..{self.hi} bases, "
+                f"{self.k}-mers")
+
+
+DNA_WORKLOADS = {
+    # transcript-length slab: the mRNA workload's length range, 65,536 sequences
+    "k1": DnaWorkload("k1", 11, "gencode-slab-6mer", 65536, 500, 2048),
+    # a handful of long sequences (chromosome-scale runs)
+    "k2": DnaWorkload("k2", 12, "long-6mer", 8, 1 << 20, 1 << 22),
+}
+
+
+def dna(seed, cfg, batch, lo, hi, n_rate=1e-3, soft_rate=0.1):
+    """Returns (bases uint8, starts int64 [batch + 1])."""
+    lens = np.random.default_rng([seed, cfg, 3]).integers(lo, hi + 1, size=batch)
+    starts = np.zeros(batch + 1, dtype=np.int64)
+    np.cumsum(lens, out=starts[1:])
+    total = int(starts[-1])
+    rng = np.random.default_rng([seed, cfg, 6])
+    alphabet = np.frombuffer(b"ACGT", dtype=np.uint8)
+    bases = alphabet[rng.integers(0, 4, size=total, dtype=np.uint8)]
+    if total:
+        unknown = rng.random(total) < n_rate
+        bases[unknown] = ord("N")
+        # soft-masked runs: run starts at rate soft_rate / 50, each 50 bases long
+        run_starts = np.flatnonzero(rng.random(total) < soft_rate / 50.0)
+        if run_starts.size:
+            mark = np.zeros(total + 51, dtype=np.int32)
+            np.add.at(mark, run_starts, 1)
+            np.add.at(mark, run_starts + 50, -1)
+            lower = np.cumsum(mark)[:total] > 0
+            bases[lower] = bases[lower] | 0x20
+    return bases, starts
+
+
+def make_dna(key, seed=42):
+    w = DNA_WORKLOADS[key]
+    bases, starts = dna(seed, w.cfg, w.batch, w.lo, w.hi)
+    lens = np.diff(starts)
+    windows = int(max(0, lens.max() - w.k + 1))
+    n_out = (windows + BLOCK - 1) // BLOCK * BLOCK
+    return dict(workload=w, bases=bases, starts=starts, n_out=n_out)

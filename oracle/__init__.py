@@ -11,7 +11,8 @@ GPU consumes; results are float64.  The computation follows the NucleoByte
 project page, section 3 ("Localized Block-Sparse Attention Matrix" for the
 band rule, "Softmax Normalization & Online Numerical Stability" for the scores
 and the softmax, "Custom Backpropagation" for the gradients); see orc.c for
-the definitions.
+the definitions.  ``kmer_tokenize`` follows the same page's section 2, item 1
+("Fused 2-Bit Tokenization"), with the 6-mer vocabulary of section 5.
 
 Parity pins (what ties each routine to something other than itself) live in
 ``tests/test_oracle_*.py``.  No oracle routine is "parity unpinned".
@@ -53,7 +54,9 @@ def _declare(lib):
     lib.orc_backward_blocks_f64.argtypes = [i, i, i, i, i, i, i, ctypes.c_double, _i32p, _f32p,
                                             _f32p, _f32p, _f32p, ctypes.c_int64, _i32p, _f64p,
                                             _f64p, _f64p, i]
-    for name in ("orc_active_blocks", "orc_masks", "orc_forward_f64", "orc_forward_blocks_f64",
+    lib.orc_kmer_tokenize.argtypes = [i, ctypes.POINTER(ctypes.c_uint8),
+                                      ctypes.POINTER(ctypes.c_int64), i, i, _i32p, _i32p]
+    for name in ("orc_kmer_tokenize", "orc_active_blocks", "orc_masks", "orc_forward_f64", "orc_forward_blocks_f64",
                  "orc_forward_recurrence_f64", "orc_backward_f64", "orc_backward_blocks_f64"):
         getattr(lib, name).restype = i
     return lib
@@ -228,3 +231,29 @@ def backward_blocks(q, k, v, dout, sel, seqlens=None, bsize=32, radius=1, causal
                                        _ptr(dv, _f64p), nthreads or default_threads()),
            "orc_backward_blocks_f64")
     return dq, dk, dv
+
+
+def kmer_specials(k=6):
+    """Special IDs after the 4^k k-mer IDs: PAD, MASK, UNK (4^k + 3 is reserved)."""
+    four_k = 4 ** k
+    return dict(pad=four_k, mask=four_k + 1, unk=four_k + 2, vocab=four_k + 4)
+
+
+def kmer_tokenize(bases, starts, k=6, n_out=None, lib=None):
+    """Sliding-window k-mer IDs.  ``bases`` uint8 (the sequences' ASCII bytes
+    back to back), ``starts`` int64 [batch + 1] byte offsets.  Returns (ids
+    int32 [batch, n_out], ntok int32 [batch]); ``n_out`` defaults to the longest
+    sequence's window count."""
+    lib = lib or load()
+    bases = np.ascontiguousarray(bases, dtype=np.uint8)
+    starts = np.ascontiguousarray(starts, dtype=np.int64)
+    batch = starts.shape[0] - 1
+    if n_out is None:
+        n_out = int(max(0, (np.diff(starts) - k + 1).max(initial=0)))
+    ids = np.full((batch, n_out), -7, dtype=np.int32)
+    ntok = np.full(batch, -7, dtype=np.int32)
+    bp = bases.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)) if bases.size else None
+    _check(lib.orc_kmer_tokenize(batch, bp, starts.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                 k, n_out, _ptr(ids, _i32p), _ptr(ntok, _i32p)),
+           "orc_kmer_tokenize")
+    return ids, ntok

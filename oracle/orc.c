@@ -42,6 +42,19 @@
  * with t over valid rows and s over A(b,t); padded rows and keys get zero.
  * O and P are recomputed here from Q, K, V in double (the exact forward).
  *
+ * orc_kmer_tokenize follows the same page's section 2, item 1 ("Fused 2-Bit
+ * Tokenization") and section 1 ("Token Blur": a hard-coded, bit-packed sliding
+ * window instead of a learned vocabulary), with the k-mer size and vocabulary of
+ * section 5 (6-mers, 4096 k-mer IDs plus padding/mask entries; the usage example
+ * of section 6 builds the model with 4100 entries).  Each base is two bits
+ * (A = 0, C = 1, G = 2, T = 3, first base most significant); the page's printed
+ * IDs (TGGGAC = 3745, TGAAGT = 3595, GGCCCC = 2645) fix that code.  Window t of
+ * a sequence covers bases t .. t+k-1 (stride one: a sliding window); its ID is
+ *     id_t = sum_{p=0}^{k-1} code(base[t+p]) * 4^(k-1-p),
+ * or UNK when one of its bases is not A, C, G or T (either case).  Rows are
+ * padded to n_out tokens with PAD.  Special IDs: PAD = 4^k, MASK = 4^k + 1,
+ * UNK = 4^k + 2, 4^k + 3 reserved (4^k + 4 entries: 4100 for k = 6).
+ *
  * Inputs are float (the exact bf16- or fp32-rounded values a GPU consumes);
  * every product and sum is taken in double.  Q, K, V, O are [batch][heads][n][d]
  * contiguous.  All routines return 0 on success and a negative code on bad
@@ -732,4 +745,66 @@ int orc_backward_blocks_f64(int batch, int heads, int n, int d, int bsize, int r
     jb.dk = dk;
     jb.dv = dv;
     return run_bpool(&jb, nthreads);
+}
+
+/* ------------------------------------------------------------------ k-mers */
+
+/* The two-bit code of one base, or -1 for anything that is not a base. */
+static int base_code(uint8_t c)
+{
+    switch (c) {
+    case 'A': case 'a': return 0;
+    case 'C': case 'c': return 1;
+    case 'G': case 'g': return 2;
+    case 'T': case 't': return 3;
+    default: return -1;
+    }
+}
+
+/* bases: the sequences' ASCII bytes back to back; starts[batch + 1]: sequence b
+ * is bytes [starts[b], starts[b+1]).  ids [batch][n_out] receives window IDs
+ * (PAD past the sequence's last window), ntok[batch] the number of windows
+ * written: min(max(len - k + 1, 0), n_out). */
+int orc_kmer_tokenize(int batch, const uint8_t *bases, const int64_t *starts, int k, int n_out,
+                      int32_t *ids, int32_t *ntok)
+{
+    if (batch < 0 || k < 1 || k > 12 || n_out < 0 || !starts || (batch > 0 && (!ids || !ntok)))
+        return ORC_E_INVALID;
+    if (starts[0] < 0)
+        return ORC_E_INVALID;
+    for (int b = 0; b < batch; ++b)
+        if (starts[b + 1] < starts[b])
+            return ORC_E_INVALID;
+    if (batch > 0 && starts[batch] > starts[0] && !bases)
+        return ORC_E_INVALID;
+    const int32_t four_k = 1 << (2 * k);
+    const int32_t pad = four_k, unk = four_k + 2;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t len = starts[b + 1] - starts[b];
+        int64_t nt = len - k + 1;
+        if (nt < 0)
+            nt = 0;
+        if (nt > n_out)
+            nt = n_out;
+        ntok[b] = (int32_t)nt;
+        const uint8_t *seq = bases + starts[b];
+        for (int64_t t = 0; t < n_out; ++t) {
+            int32_t id = pad;
+            if (t < nt) {
+                int64_t value = 0, place = 1;
+                int bad = 0;
+                for (int p = k - 1; p >= 0; --p) {   /* last base is the least significant */
+                    const int c = base_code(seq[t + p]);
+                    if (c < 0)
+                        bad = 1;
+                    else
+                        value += c * place;
+                    place *= 4;
+                }
+                id = bad ? unk : (int32_t)value;
+            }
+            ids[(int64_t)b * n_out + t] = id;
+        }
+    }
+    return 0;
 }

@@ -197,3 +197,80 @@ def test_backward_mutant_is_caught(name):
         lib_path = obuild.build(out=os.path.join(tmp, "liborc_mutant.so"), src=path)
         lib = oracle.load(lib_path)
         assert _bwd_battery(lib) != [], f"mutant {name} slipped through every pin"
+
+
+# ------------------------------------------------------------ k-mer tokenizer
+
+KMER_MUTANTS = {
+    "kmer_lsb_first": ("for (int p = k - 1; p >= 0; --p) {", "for (int p = 0; p < k; ++p) {"),
+    "kmer_swap_c_g": ("case 'C': case 'c': return 1;\n    case 'G': case 'g': return 2;",
+                      "case 'C': case 'c': return 2;\n    case 'G': case 'g': return 1;"),
+    "kmer_unknown_ignored": ("id = bad ? unk : (int32_t)value;",
+                             "id = (bad && 0) ? unk : (int32_t)value;"),
+    "kmer_count_off_by_one": ("int64_t nt = len - k + 1;", "int64_t nt = len - k;"),
+    "kmer_case_sensitive": ("case 'A': case 'a': return 0;", "case 'A': return 0;"),
+    "kmer_pad_zero": ("int32_t id = pad;", "int32_t id = 0 * pad;"),
+    "kmer_window_shift": ("const int c = base_code(seq[t + p]);",
+                          "const int c = base_code(seq[t + p + (t > 0)]);"),
+}
+
+
+def _kmer_battery(lib):
+    failed = []
+    here = os.path.dirname(os.path.abspath(__file__))
+
+    def tok(text, k=6, n_out=None):
+        b = np.frombuffer(text, dtype=np.uint8)
+        return oracle.kmer_tokenize(b, np.array([0, len(b)]), k, n_out, lib=lib)
+    try:
+        with open(os.path.join(here, "golden", "kmer_page_ids.txt")) as f:
+            for line in f:
+                if line.strip() and not line.startswith("#"):
+                    kmer, ident = line.split()
+                    if tok(kmer.encode())[0][0, 0] != int(ident):
+                        failed.append("page_ids")
+        import itertools
+        kmers = "".join("".join(t) for t in itertools.product("ACGT", repeat=3)).encode()
+        ids, _ = oracle.kmer_tokenize(np.frombuffer(kmers, np.uint8),
+                                      np.arange(65, dtype=np.int64) * 3, 3, lib=lib)
+        if not np.array_equal(ids[:, 0], np.arange(64)):
+            failed.append("lexicographic")
+        rng = np.random.default_rng(3)
+        text = rng.choice(list(b"ACGT"), 200).astype(np.uint8).tobytes()
+        ids, nt = tok(text)
+        code = {65: 0, 67: 1, 71: 2, 84: 3}
+        if nt[0] != 195:
+            failed.append("count")
+        row = ids[0].astype(np.int64)
+        if any(row[t + 1] != (row[t] % 1024) * 4 + code[text[t + 6]] for t in range(min(nt[0], 195) - 1)):
+            failed.append("sliding")
+        ids, nt = tok(b"ACGTACGTACGTNACGTACGTAC", 6, 32)
+        unk = [t for t in range(nt[0]) if ids[0, t] == 4098]
+        if unk != list(range(7, 13)):
+            failed.append("unknown")
+        if not np.all(ids[0, nt[0]:] == 4096):
+            failed.append("pad")
+        if not np.array_equal(tok(b"acgtacgtacgtnacgtacgtac", 6, 32)[0], ids):
+            failed.append("case")
+    except oracle.OracleError:
+        failed.append("error")
+    return sorted(set(failed))
+
+
+def test_unmodified_oracle_passes_kmer_battery():
+    assert _kmer_battery(oracle.load()) == []
+
+
+@pytest.mark.parametrize("name", sorted(KMER_MUTANTS))
+def test_kmer_mutant_is_caught(name):
+    old, new = KMER_MUTANTS[name]
+    with open(obuild.SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "orc_mutant.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        lib_path = obuild.build(out=os.path.join(tmp, "liborc_mutant.so"), src=path)
+        lib = oracle.load(lib_path)
+        assert _kmer_battery(lib) != [], f"mutant {name} slipped through every pin"
