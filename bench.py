@@ -297,6 +297,80 @@ def cpu_baseline(r, target_flops=1.0e12, log=print):
             "seconds": dt}
 
 
+def time_kmer(key, steps, warmup, log=print):
+    """The fused k-mer tokenizer (bsl_kmer_tokenize) on a seeded nucleotide
+    workload resident in HBM: text, offsets, padded int32 ID rows, counts."""
+    import torch
+    from block_sparse_local_amd import bsl, inputs
+
+    t0 = time.time()
+    d = inputs.make_dna(key, 42)
+    w = d["workload"]
+    log(f"[bench] {key} text drawn in {time.time() - t0:.1f}s: {w.describe()}, "
+        f"{len(d['bases'])} bytes, rows of {d['n_out']}")
+    bases = torch.from_numpy(d["bases"]).cuda()
+    starts = torch.from_numpy(d["starts"]).cuda()
+    batch, n_out = w.batch, d["n_out"]
+    ids = torch.empty((batch, n_out), dtype=torch.int32, device="cuda")
+    ntok = torch.empty(batch, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        bsl.kmer_tokenize(bases, starts, w.k, n_out, ids=ids, ntok=ntok, stream=stream)
+    torch.cuda.synchronize()
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t_begin = time.perf_counter()
+    for s in range(steps):
+        ev0[s].record(stream)
+        bsl.kmer_tokenize(bases, starts, w.k, n_out, ids=ids, ntok=ntok, stream=stream)
+        ev1[s].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_begin
+    per_launch = np.array([a.elapsed_time(b) * 1e-3 for a, b in zip(ev0, ev1)])
+    windows = int(ntok.sum().item())
+    del bases, starts, ids, ntok
+    torch.cuda.empty_cache()
+    # algorithmic bytes: the text read once, the offsets, every ID row element
+    # and every count written once
+    alg = len(d["bases"]) + 8 * (batch + 1) + 4 * batch * n_out + 4 * batch
+    mean = float(per_launch.mean())
+    t_step = wall / steps
+    roof = {"bound": "hbm", "achieved": alg / mean / 1e9, "peak": 8000.0, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    out = {"config": {"workload": f"{key} {w.describe()}", "sequences": batch,
+                      "bases": int(len(d["bases"])), "k": w.k, "n_out": n_out,
+                      "windows": windows},
+           "metric": "k-mer tokens/s", "value": windows / t_step, "unit": "tokens/s",
+           "ms_per_step": t_step * 1e3, "roofline": roof,
+           "detail": {"mean_launch_us": mean * 1e6,
+                      "median_launch_us": float(np.median(per_launch)) * 1e6,
+                      "alg_bytes": alg, "windows": windows}}
+    log(f"[bench] {key} tokenizer: {t_step * 1e3:.3f} ms/step, {windows / t_step / 1e9:.2f} G "
+        f"windows/s, {roof['achieved']:.0f} GB/s ({roof['frac'] * 100:.1f}% of hbm peak)")
+    return out, d
+
+
+def cpu_baseline_kmer(d, log=print, target_bytes=2.0e9):
+    """The oracle tokenizer (one thread: it is a single loop) on the first
+    sequences of the same workload, about ``target_bytes`` of text."""
+    import oracle
+    w = d["workload"]
+    starts = d["starts"]
+    nseq = int(np.searchsorted(starts, target_bytes)) or 1
+    nseq = min(nseq, w.batch)
+    sub = starts[:nseq + 1]
+    text = d["bases"][:int(sub[-1])]
+    t0 = time.perf_counter()
+    _, nt = oracle.kmer_tokenize(text, sub, w.k, d["n_out"])
+    dt = time.perf_counter() - t0
+    windows = int(nt.sum())
+    log(f"[bench] oracle tokenizer: {nseq} sequences, {windows} windows in {dt:.1f}s")
+    return {"value": windows / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {nseq} of {w.batch} sequences ({len(text)} bases, "
+                      f"{windows} windows), one thread", "seconds": dt}
+
+
 def summarize(r, traffic=None):
     acc, w = r["acc"], r["w"]
     t_step = r["wall"] / r["steps"]
@@ -353,6 +427,9 @@ def main():
                     help="also time the backward pass (bsl_backward) on the same workload")
     ap.add_argument("--varlen", action="store_true",
                     help="also time the same workload in the packed layout (bsl_forward_varlen)")
+    ap.add_argument("--kmer", action="store_true",
+                    help="also time the fused k-mer tokenizer (bsl_kmer_tokenize)")
+    ap.add_argument("--kmer-workload", default="k1", choices=["k1", "k2"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 1 GiB device copies (for counter calibration)")
     args = ap.parse_args()
@@ -444,6 +521,11 @@ def main():
         log(f"[bench] {args.workload} backward: {tb * 1e3:.3f} ms/step, "
             f"{extrab['useful_tflops']:.1f} useful TFLOP/s ({roofb['frac'] * 100:.1f}% of "
             f"{roofb['bound']} peak)")
+    if args.kmer:
+        kout, kd = time_kmer(args.kmer_workload, args.steps, args.warmup, log)
+        if not args.no_cpu_baseline:
+            kout["cpu_baseline"] = cpu_baseline_kmer(kd, log=log)
+        line["kmer"] = kout
     print(json.dumps(line), flush=True)
 
 

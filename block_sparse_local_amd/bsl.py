@@ -24,7 +24,8 @@ BSL_BF16, BSL_F32 = 0, 1
 
 # every function include/bsl.h declares
 EXPORTS = ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_forward_varlen",
-           "bsl_varlen_offsets", "bsl_backward", "bsl_destroy", "bsl_status_string",
+           "bsl_varlen_offsets", "bsl_backward", "bsl_kmer_tokenize", "bsl_kmer_ceiling",
+           "bsl_destroy", "bsl_status_string",
            "bsl_last_error", "bsl_version")
 
 
@@ -71,6 +72,8 @@ def load(path=LIB_PATH):
     i32p = ctypes.POINTER(i32)
     lib.bsl_varlen_offsets.argtypes = [i32, i32p, i32p, i32p, i32p]
     lib.bsl_backward.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.bsl_kmer_tokenize.argtypes = [i32, vp, ctypes.c_int64, vp, i32, i32, vp, vp, vp]
+    lib.bsl_kmer_ceiling.argtypes = [i32, ctypes.POINTER(ctypes.c_int64), i32, ctypes.POINTER(i32)]
     lib.bsl_destroy.argtypes = [vp]
     lib.bsl_status_string.argtypes = [ctypes.c_int]
     lib.bsl_status_string.restype = ctypes.c_char_p
@@ -79,7 +82,8 @@ def load(path=LIB_PATH):
     lib.bsl_version.argtypes = []
     lib.bsl_version.restype = i32
     for name in ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_forward_varlen",
-                 "bsl_varlen_offsets", "bsl_backward", "bsl_destroy"):
+                 "bsl_varlen_offsets", "bsl_backward", "bsl_kmer_tokenize", "bsl_kmer_ceiling",
+                 "bsl_destroy"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -153,6 +157,55 @@ def bsl_backward(plan, batch, n, q, k, v, o, dout, lse, seqlens, dq, dk, dv, del
     _check(load().bsl_backward(plan, batch, n, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
                                _ptr(lse), _ptr(seqlens), _ptr(dq), _ptr(dk), _ptr(dv),
                                _ptr(delta), _stream(stream)))
+
+
+def bsl_kmer_tokenize(batch, bases, nbytes, starts, k, n_out, ids, ntok=None, stream=None):
+    _check(load().bsl_kmer_tokenize(batch, _ptr(bases), nbytes, _ptr(starts), k, n_out, _ptr(ids),
+                                    _ptr(ntok), _stream(stream)))
+
+
+def bsl_kmer_ceiling(starts, k=6):
+    """Host int64 starts [batch + 1] -> the padded row width (a multiple of 32)."""
+    import numpy as np
+    st = np.ascontiguousarray(starts, dtype=np.int64)
+    if st.ndim != 1 or st.shape[0] < 1:
+        raise ValueError("starts must be one-dimensional with batch + 1 entries")
+    out = ctypes.c_int32()
+    _check(load().bsl_kmer_ceiling(st.shape[0] - 1, st.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                   k, ctypes.byref(out)))
+    return out.value
+
+
+def kmer_specials(k=6):
+    """The special IDs after the 4^k k-mer IDs (BSL_KMER_* in include/bsl.h)."""
+    pad = 1 << (2 * k)
+    return dict(pad=pad, mask=pad + 1, unk=pad + 2, vocab=pad + 4)
+
+
+def kmer_tokenize(bases, starts, k=6, n_out=None, ids=None, ntok=None, stream=None):
+    """bases: uint8 CUDA tensor (the text); starts: int64 CUDA tensor [batch + 1].
+    Returns (ids int32 [batch, n_out], ntok int32 [batch]); ``n_out`` is
+    required (bsl_kmer_ceiling computes it from host offsets)."""
+    import torch
+    if bases.dtype != torch.uint8 or not bases.is_cuda or bases.dim() != 1:
+        raise ValueError("bases must be a one-dimensional uint8 CUDA tensor")
+    if starts.dtype != torch.int64 or not starts.is_cuda or starts.dim() != 1 or starts.shape[0] < 1:
+        raise ValueError("starts must be an int64 CUDA tensor of shape [batch + 1]")
+    if not bases.is_contiguous() or not starts.is_contiguous():
+        raise ValueError("bases and starts must be contiguous")
+    if n_out is None:
+        raise ValueError("n_out is required (bsl_kmer_ceiling gives it from host offsets)")
+    batch = starts.shape[0] - 1
+    if ids is None:
+        ids = torch.empty((batch, n_out), dtype=torch.int32, device=bases.device)
+    if ntok is None:
+        ntok = torch.empty(batch, dtype=torch.int32, device=bases.device)
+    if ids.dtype != torch.int32 or ids.shape != (batch, n_out) or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous int32 tensor of shape [batch, n_out]")
+    if ntok.dtype != torch.int32 or ntok.shape != (batch,) or not ntok.is_contiguous():
+        raise ValueError("ntok must be a contiguous int32 tensor of shape [batch]")
+    bsl_kmer_tokenize(batch, bases, bases.numel(), starts, k, n_out, ids, ntok, stream)
+    return ids, ntok
 
 
 def bsl_destroy(plan):

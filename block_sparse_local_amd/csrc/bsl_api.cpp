@@ -388,3 +388,78 @@ const char *bsl_last_error(void) { return g_last_error; }
 int32_t bsl_version(void) { return BSL_VERSION; }
 
 } // extern "C"
+
+extern "C" {
+
+bsl_status bsl_kmer_tokenize(int32_t batch, const uint8_t *bases, int64_t nbytes,
+                             const int64_t *starts, int32_t k, int32_t n_out, int32_t *ids,
+                             int32_t *ntok, void *stream)
+{
+    if (batch < 0 || nbytes < 0 || n_out < 0)
+        return fail(BSL_E_INVALID, "batch (%d), nbytes (%lld) and n_out (%d) must be >= 0", batch,
+                    (long long)nbytes, n_out);
+    if (k < 1 || k > 12)
+        return fail(BSL_E_INVALID, "k must be in 1 .. 12 (got %d)", k);
+    if (batch == 0)
+        return BSL_OK;
+    if (!starts || (n_out > 0 && !ids) || (nbytes > 0 && !bases))
+        return fail(BSL_E_INVALID, "bases, starts and ids must be non-NULL device pointers");
+    const long long tiles = bsl::kmer_tiles(n_out);
+    if ((long long)batch * (tiles > 0 ? tiles : 1) > 0x7fffffffLL)
+        return fail(BSL_E_INVALID, "batch x tiles of the launch exceeds 2^31 - 1");
+    const size_t id_bytes = (size_t)batch * (size_t)n_out * 4u;
+    const size_t st_bytes = ((size_t)batch + 1u) * 8u;
+    if (overlaps(ids, id_bytes, starts, st_bytes) ||
+        (nbytes > 0 && overlaps(ids, id_bytes, bases, (size_t)nbytes)))
+        return fail(BSL_E_INVALID, "ids overlaps bases or starts");
+    if (ntok && (overlaps(ntok, (size_t)batch * 4u, starts, st_bytes) ||
+                 (nbytes > 0 && overlaps(ntok, (size_t)batch * 4u, bases, (size_t)nbytes)) ||
+                 overlaps(ntok, (size_t)batch * 4u, ids, id_bytes)))
+        return fail(BSL_E_INVALID, "ntok overlaps bases, starts or ids");
+    bsl::KmerLaunch a;
+    a.bases = bases;
+    a.nbytes = nbytes;
+    a.starts = starts;
+    a.ids = ids;
+    a.ntok = ntok;
+    a.batch = batch;
+    a.k = k;
+    a.n_out = n_out;
+    a.stream = (hipStream_t)stream;
+    if (n_out == 0) {
+        if (!ntok)
+            return BSL_OK;
+        // only the counts: one workgroup per sequence, no windows
+        a.n_out = 0;
+    }
+    const hipError_t e = bsl::launch_kmer(a);
+    if (e != hipSuccess)
+        return fail(BSL_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    return BSL_OK;
+}
+
+bsl_status bsl_kmer_ceiling(int32_t batch, const int64_t *starts, int32_t k, int32_t *n_out)
+{
+    if (batch < 0)
+        return fail(BSL_E_INVALID, "batch must be >= 0 (got %d)", batch);
+    if (k < 1 || k > 12)
+        return fail(BSL_E_INVALID, "k must be in 1 .. 12 (got %d)", k);
+    if (!starts || !n_out)
+        return fail(BSL_E_INVALID, "starts and n_out must be non-NULL");
+    if (starts[0] < 0)
+        return fail(BSL_E_INVALID, "starts[0] = %lld is negative", (long long)starts[0]);
+    long long mx = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        if (starts[b + 1] < starts[b])
+            return fail(BSL_E_INVALID, "starts decreases at %d", b);
+        const long long w = (long long)(starts[b + 1] - starts[b]) - k + 1;
+        mx = w > mx ? w : mx;
+    }
+    const long long ceil32 = (mx + 31) / 32 * 32;
+    if (ceil32 > 0x7fffffffLL)
+        return fail(BSL_E_INVALID, "the longest window count rounds up past 2^31 - 1");
+    *n_out = (int32_t)ceil32;
+    return BSL_OK;
+}
+
+} // extern "C"

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define BSL_VERSION 10200 /* major * 10000 + minor * 100 + patch */
+#define BSL_VERSION 10300 /* major * 10000 + minor * 100 + patch */
 
 typedef enum bsl_status {
     BSL_OK = 0,
@@ -187,6 +187,61 @@ bsl_status bsl_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
                         const void *k, const void *v, const void *o, const void *dout,
                         const float *lse, const int32_t *seqlens, void *dq, void *dk, void *dv,
                         float *delta, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Fused 2-bit k-mer tokenization: the step that feeds the model's token IDs
+ * (NucleoByte project page, section 2, item 1, "Fused 2-Bit Tokenization"; the
+ * k-mer size and vocabulary are those of section 5: 6-mers, 4096 IDs plus
+ * padding and mask entries, 4100 in the usage example of section 6).
+ *
+ * Each base is two bits: A = 0, C = 1, G = 2, T = 3, upper or lower case (soft-
+ * masked FASTA text).  Window t of a sequence covers bases t .. t+k-1 (a
+ * sliding window, stride one) and its ID is the base-4 number of its codes,
+ * first base most significant:  id_t = sum_p code(base[t+p]) * 4^(k-1-p)  (the
+ * page prints TGGGAC = 3745, TGAAGT = 3595, GGCCCC = 2645).  A window that
+ * holds any other byte ('N', IUPAC codes, line breaks) is UNK.  The special
+ * IDs follow the 4^k k-mer IDs: */
+#define BSL_KMER_PAD(k) (1 << (2 * (k)))        /* rows past a sequence's last window */
+#define BSL_KMER_MASK(k) (BSL_KMER_PAD(k) + 1)  /* reserved for masked-token training */
+#define BSL_KMER_UNK(k) (BSL_KMER_PAD(k) + 2)   /* a window holding a non-base byte */
+#define BSL_KMER_VOCAB(k) (BSL_KMER_PAD(k) + 4) /* one more ID reserved: 4100 at k = 6 */
+
+/* Enqueue the tokenization of a batch of sequences into padded rows of IDs.
+ *   batch   >= 0 sequences.
+ *   bases   device uint8[nbytes]: the sequences' text back to back (sequence
+ *           bodies only: no FASTA headers; a line break inside a sequence is a
+ *           non-base and makes its windows UNK).  Any alignment.
+ *   nbytes  >= 0, the size of bases: no byte at or past it is read.
+ *   starts  device int64[batch + 1]: sequence b is bytes [starts[b],
+ *           starts[b+1]).  Values are clamped into [0, nbytes] on the device
+ *           and a decreasing pair gives an empty sequence, so no value can send
+ *           an access outside the buffer.
+ *   k       1 .. 12 bases per window (6 on the page).
+ *   n_out   >= 0 windows per output row (the dynamic ceiling of section 2,
+ *           item 2: bsl_kmer_ceiling gives the longest window count rounded up
+ *           to a multiple of 32, the n bsl_forward takes).
+ *   ids     device int32[batch][n_out]: row b, column t holds window t's ID,
+ *           BSL_KMER_PAD(k) for t >= ntok[b].  Every element is written.
+ *   ntok    device int32[batch] or NULL: the windows written for sequence b,
+ *           min(max(len_b - k + 1, 0), n_out) (the sequence lengths bsl_forward
+ *           takes for the model's activations).
+ *   stream  a hipStream_t, or NULL for the default stream.
+ * batch == 0 is a no-op returning BSL_OK; with n_out == 0 only ntok is written
+ * (ids may then be NULL).  BSL_E_INVALID for a NULL bases (when nbytes > 0),
+ * starts or ids (when n_out > 0), negative sizes, k outside 1 .. 12, ids or ntok
+ * overlapping the inputs or each other, or a launch of 2^31 or more
+ * workgroups; BSL_E_DEVICE if the launch fails.  Nothing is written when an
+ * argument error is returned. */
+bsl_status bsl_kmer_tokenize(int32_t batch, const uint8_t *bases, int64_t nbytes,
+                             const int64_t *starts, int32_t k, int32_t n_out, int32_t *ids,
+                             int32_t *ntok, void *stream);
+
+/* Host-side row width for bsl_kmer_tokenize: from host int64 starts[batch + 1]
+ * (non-decreasing, starts[0] >= 0), *n_out = the longest sequence's window
+ * count (len - k + 1, at least 0) rounded up to a multiple of 32.  No device
+ * work.  BSL_E_INVALID for batch < 0, a NULL pointer, k outside 1 .. 12,
+ * decreasing or negative offsets, or a result past 2^31 - 1. */
+bsl_status bsl_kmer_ceiling(int32_t batch, const int64_t *starts, int32_t k, int32_t *n_out);
 
 /* Release a plan.  NULL is accepted and ignored.  Do not call while work
  * enqueued with the plan is being launched from another thread. */

@@ -153,3 +153,29 @@ def test_library_override_is_loud_when_missing(tmp_path):
                        text=True, timeout=300)
     assert r.returncode == 3, r.stdout + r.stderr
     assert str(missing) in r.stdout
+
+
+def test_kmer_ceiling_host():
+    import numpy as np
+    assert bsl.bsl_kmer_ceiling(np.array([0, 100, 2100]), 6) == 2016
+    assert bsl.bsl_kmer_ceiling(np.array([0, 3]), 6) == 0
+    assert bsl.bsl_kmer_ceiling(np.array([0, 38]), 6) == 64
+    assert bsl.bsl_kmer_ceiling(np.array([7]), 6) == 0
+    for starts, k in (([5, 3], 6), ([-1, 3], 6), ([0, 8], 0), ([0, 8], 13)):
+        with pytest.raises(bsl.BslError):
+            bsl.bsl_kmer_ceiling(np.array(starts), k)
+
+
+def test_kmer_argument_errors_before_any_launch(lib):
+    """Rejected before anything touches a device (these run without a GPU)."""
+    bad = [(-1, 1, 8, 6, 8), (2, -1, 8, 6, 8), (2, 8, 8, 0, 8), (2, 8, 8, 13, 8),
+           (2, 8, 8, 6, -1)]
+    for batch, nbytes, st, k, n_out in bad:
+        assert lib.bsl_kmer_tokenize(batch, 4096, nbytes, 8192, k, n_out, 16384, None, None) == 1
+    # NULL starts or ids
+    assert lib.bsl_kmer_tokenize(2, 4096, 8, None, 6, 8, 16384, None, None) == 1
+    assert lib.bsl_kmer_tokenize(2, 4096, 8, 8192, 6, 8, None, None, None) == 1
+    # ids overlapping the text
+    assert lib.bsl_kmer_tokenize(2, 4096, 100, 8192, 6, 8, 4100, None, None) == 1
+    # batch 0 is a no-op
+    assert lib.bsl_kmer_tokenize(0, None, 0, None, 6, 8, None, None, None) == 0
