@@ -19,7 +19,8 @@
 //    it needs as aligned LDS dwords, realigns them with v_alignbyte, computes
 //    each base's code ((x >> 1) ^ (x >> 2)) & 3 -- the low bits of the ASCII
 //    letters, case included -- and its validity, rolls the window ID along the
-//    8 windows and writes them as two 16-byte stores.
+//    8 windows and writes them as two 16-byte stores -- streaming (non-
+//    temporal) stores when the output is larger than half the Infinity Cache.
 #include "launch.h"
 
 #include <hip/hip_runtime.h>
@@ -47,7 +48,7 @@ __device__ __forceinline__ bool is_base(uint32_t x)
 
 __device__ __forceinline__ uint32_t base_code(uint32_t x) { return ((x >> 1) ^ (x >> 2)) & 3u; }
 
-template <int K>
+template <int K, bool STREAM>
 __global__ void __launch_bounds__(TPB) kmer_kernel(KmerLaunch a, int tiles)
 {
     __shared__ __attribute__((aligned(16))) uint32_t stage[STAGE_BYTES / 4];
@@ -139,8 +140,16 @@ __global__ void __launch_bounds__(TPB) kmer_kernel(KmerLaunch a, int tiles)
     }
     int32_t *row = a.ids + (int64_t)b * a.n_out;
     if (j0 + TPT <= a.n_out && (((uintptr_t)(row + j0)) & 15u) == 0) {
-        *(i32x4 *)(row + j0) = i32x4{id[0], id[1], id[2], id[3]};
-        *(i32x4 *)(row + j0 + 4) = i32x4{id[4], id[5], id[6], id[7]};
+        const i32x4 lo4 = {id[0], id[1], id[2], id[3]}, hi4 = {id[4], id[5], id[6], id[7]};
+        if (STREAM) {
+            // streaming stores: an output too large for the last-level cache
+            // would only evict the text from it
+            __builtin_nontemporal_store(lo4, (i32x4 *)(row + j0));
+            __builtin_nontemporal_store(hi4, (i32x4 *)(row + j0 + 4));
+        } else {
+            *(i32x4 *)(row + j0) = lo4;
+            *(i32x4 *)(row + j0 + 4) = hi4;
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < TPT; ++j)
@@ -149,10 +158,21 @@ __global__ void __launch_bounds__(TPB) kmer_kernel(KmerLaunch a, int tiles)
     }
 }
 
+// Outputs past this size leave with streaming stores (MI355X's last-level
+// cache, the Infinity Cache, holds 256 MB; a smaller output stays there for the
+// embedding lookup that reads it next).
+constexpr size_t STREAM_BYTES = (size_t)128 << 20;
+
 template <int K>
 hipError_t launch_k(const KmerLaunch &a, int tiles)
 {
-    hipLaunchKernelGGL(kmer_kernel<K>, dim3(a.batch * tiles), dim3(TPB), 0, a.stream, a, tiles);
+    const bool stream = (size_t)a.batch * (size_t)a.n_out * 4u > STREAM_BYTES;
+    if (stream)
+        hipLaunchKernelGGL((kmer_kernel<K, true>), dim3(a.batch * tiles), dim3(TPB), 0, a.stream, a,
+                           tiles);
+    else
+        hipLaunchKernelGGL((kmer_kernel<K, false>), dim3(a.batch * tiles), dim3(TPB), 0, a.stream,
+                           a, tiles);
     return hipGetLastError();
 }
 
