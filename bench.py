@@ -81,27 +81,35 @@ def code_text(src):
     return _scan(bare, False, lambda ws: "\n" if "\n" in ws else " ").strip()
 
 
+KMER_SOURCES = ["block_sparse_local_amd/csrc/kmer.hip", "block_sparse_local_amd/csrc/launch.h"]
+
+
 def kernel_sha():
     """Hash of the bf16 kernel's code (comments and layout excluded)."""
+    return code_sha(KERNEL_SOURCES)
+
+
+def code_sha(sources):
+    """Hash of the code of the given sources (comments and layout excluded)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             h.update(code_text(f.read()).encode("utf-8"))
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload_key):
+def stored_traffic(workload_key, kernel="fwd_bf16", sources=None):
     """Bytes per launch from the committed counter summary, if it was taken on
     the current kernel code."""
     if os.environ.get("BSL_LIBRARY"):
         return None  # the stored counters describe the in-tree build only
-    path = os.path.join(ROOT, "profiles", f"pmc_traffic_fwd_bf16_{workload_key}.txt")
+    path = os.path.join(ROOT, "profiles", f"pmc_traffic_{kernel}_{workload_key}.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     sha = re.search(r"^kernel_code_sha256_16:\s*(\w+)", text, re.M)
     val = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
-    if not sha or not val or sha.group(1) != kernel_sha():
+    if not sha or not val or sha.group(1) != code_sha(sources or KERNEL_SOURCES):
         return None
     return float(val.group(1))
 
@@ -337,7 +345,7 @@ def time_kmer(key, steps, warmup, log=print):
     t_step = wall / steps
     roof = {"bound": "hbm", "achieved": alg / mean / 1e9, "peak": 8000.0, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = stored_traffic(key, "kmer", KMER_SOURCES)
     out = {"config": {"workload": f"{key} {w.describe()}", "sequences": batch,
                       "bases": int(len(d["bases"])), "k": w.k, "n_out": n_out,
                       "windows": windows},
