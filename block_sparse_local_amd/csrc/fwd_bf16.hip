@@ -15,7 +15,8 @@
 //    The workgroup sweeps the union of their bands, one key block per step; each
 //    K/V block is brought into LDS once and serves every wave whose band covers
 //    it (up to 2R+1 of them).
-//  * K and V blocks travel HBM -> LDS with direct-to-LDS loads (no registers),
+//  * K and V blocks travel HBM -> LDS with direct-to-LDS buffer loads (no
+//    registers; a scalar buffer resource per block, per-lane offsets fixed),
 //    into a ring of NSTAGE buffers filled NSTAGE-1 blocks ahead of use; one
 //    barrier per step both publishes the oldest block and frees the buffer the
 //    previous step read.  16-byte chunks are XOR-swizzled per row so that the
@@ -76,6 +77,10 @@ namespace {
 #endif
 
 constexpr float RESCALE_SLACK = BSL_RESCALE_SLACK; // in log2 units
+
+// Fourth word of a raw buffer resource on gfx9-family GPUs (32-bit data
+// format, no swizzle, no index stride).
+constexpr int BUFFER_WORD3 = 0x00020000;
 
 struct Params {
     const uint16_t *q, *k, *v;
@@ -245,23 +250,44 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
     // Slot s of a stage (16 bytes at stage + 16 s) holds K (s < SLOTS/2) or V;
     // within a tile, slot -> (row, chunk position), chunk position -> logical
     // chunk through the row's swizzle.  Load u of wave w fills slots
-    // [u*NT + 64w, +64): 1 KB of LDS, 1 KB of contiguous global rows.
+    // [u*NT + 64w, +64): 1 KB of LDS, 1 KB of contiguous global rows.  The
+    // loads are buffer loads into LDS: a buffer resource (scalar registers)
+    // based at the key block's first row, plus a loop-invariant per-lane byte
+    // offset, so a step spends no vector ALU on addresses and the hardware
+    // bounds-checks every access against the block.
+    uint32_t loff[LPT];
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+        const int s = u * NT + tid;
+        const bool is_v = s >= SLOTS / 2;
+        const int t = is_v ? s - SLOTS / 2 : s;
+        const int r = t / T::CPR, cp = t % T::CPR;
+        const int c = cp ^ (is_v ? T::v_swz(r) : T::k_swz(r));
+        loff[u] = (uint32_t)r * (uint32_t)(RS * 2) + (uint32_t)c * 16u;
+    }
+    const int blk_bytes = (int)((size_t)BLK * RS * 2);
     auto issue = [&](int j, int stage) {
+        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(kg + (size_t)j * BLK * RS), (short)0, blk_bytes, BUFFER_WORD3);
+        const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(vg + (size_t)j * BLK * RS), (short)0, blk_bytes, BUFFER_WORD3);
 #pragma unroll
         for (int u = 0; u < LPT; ++u) {
-            const int s = u * NT + tid;
-            if (SLOTS < NT && s >= SLOTS)
+            if (SLOTS < NT && u * NT + wave * 64 >= SLOTS)
                 continue; // whole waves only: SLOTS is a multiple of 64
-            const bool is_v = s >= SLOTS / 2;
-            const int t = is_v ? s - SLOTS / 2 : s;
-            const int r = t / T::CPR, cp = t % T::CPR;
-            const int c = cp ^ (is_v ? T::v_swz(r) : T::k_swz(r));
-            // packed layout: rows past the end repeat the last row (in bounds;
-            // masked below); the padded buffer holds all 32 rows
-            const int row = VARLEN ? min(j * BLK + r, len - 1) : j * BLK + r;
-            const uint16_t *src = (is_v ? vg : kg) + (size_t)row * RS + c * 8;
+            const bool is_v = u * NT + wave * 64 >= SLOTS / 2; // uniform per wave
+            uint32_t off = loff[u];
+            if (VARLEN) {
+                // packed layout: rows past the end repeat the last row (in
+                // bounds; masked below); the padded buffer holds all 32 rows
+                const int t = (is_v ? u * NT + tid - SLOTS / 2 : u * NT + tid);
+                const int r = t / T::CPR;
+                const int last = len - 1 - j * BLK;
+                if (r > last)
+                    off -= (uint32_t)(r - last) * (uint32_t)(RS * 2);
+            }
             uint8_t *dst = lds + stage * STAGE + (u * NT + wave * 64) * 16;
-            __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_v ? vrs : krs, (lds_void *)dst, 16, off, 0, 0, 0);
         }
     };
 
