@@ -129,22 +129,29 @@ __device__ __forceinline__ void band_of(int x, int nb, int R, bool causal, bool 
 
 // Fill slot range of one 16 KB-or-8 KB tile pair in a ring stage: slot s of
 // the stage (16 bytes at stage + 16 s) holds tile A (s < SLOTS/2) or tile B.
+// Buffer loads into LDS: a scalar buffer resource based at the block's first
+// row of each tile (bounds-checked against the block) plus a per-lane offset
+// that does not depend on the block, so no vector ALU goes into addresses.
 template <int D, int NT, int LPT>
 __device__ __forceinline__ void issue_pair(uint8_t *stage, const uint16_t *ga, const uint16_t *gb,
                                           int row0, int tid, int wave)
 {
     using T = BTile<D>;
     constexpr int SLOTS = 2 * T::BYTES / 16;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(ga + (size_t)row0 * D), (short)0, T::BYTES, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(gb + (size_t)row0 * D), (short)0, T::BYTES, 0x00020000);
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
         const int s = u * NT + tid;
-        const bool second = s >= SLOTS / 2;
+        const bool second = u * NT + wave * 64 >= SLOTS / 2; // uniform per wave
         const int t = second ? s - SLOTS / 2 : s;
         const int r = t / T::CPR, cp = t % T::CPR;
         const int c = cp ^ T::swz(r);
-        const uint16_t *src = (second ? gb : ga) + (size_t)(row0 + r) * D + c * 8;
+        const uint32_t off = (uint32_t)(r * D + c * 8) * 2u;
         uint8_t *dst = stage + (u * NT + wave * 64) * 16;
-        __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? rb : ra, (lds_void *)dst, 16, off, 0, 0, 0);
     }
 }
 
