@@ -9,11 +9,12 @@
 // Block-Sparse Attention Matrix"; section 2, item 2).  P is recomputed from the
 // scores and the forward's stored log-sum-exp: P = exp(S - lse).
 //
-// Three kernels, in stream order:
-//  * delta: D_t in fp32 from the bf16 O and dO; 0 on padded rows.
+// Two kernels, in stream order:
 //  * dq: one wave per query block, 4 per workgroup, sweeping the union of their
 //    key bands like the forward (ring of K/V blocks filled by direct-to-LDS
-//    loads, rotated sweep, XCD-contiguous groups).  Per key block
+//    loads, rotated sweep, XCD-contiguous groups).  First D_t in fp32 from the
+//    bf16 dO fragments the wave holds anyway and the same elements of O (0 on
+//    padded rows), written out for dkv.  Then per key block
 //        S^T = K Q^T,  dP^T = V dO^T,  P^T = 2^(S^T c - lse log2 e),
 //        dS^T = P^T (dP^T - D),  dQ^T += K^T dS^T.
 //    As in the forward each lane owns one query column, so lse and D are
@@ -75,39 +76,6 @@ __device__ __forceinline__ int seq_len(const BParams &p, int b)
 {
     int len = p.seqlens ? p.seqlens[b] : p.n;
     return len < 0 ? 0 : (len > p.n ? p.n : len);
-}
-
-// --------------------------------------------------------------- delta
-// D_t = sum_c dO_tc O_tc: D/8 lanes per row, 8 bf16 each, reduced by xor
-// shuffles; 0 on rows at or past the sequence's length.
-template <int D>
-__global__ void __launch_bounds__(256) delta_kernel(BParams p)
-{
-    constexpr int LPR = D / 8;           // lanes per row
-    constexpr int RPB = 256 / LPR;       // rows per workgroup
-    const int tid = threadIdx.x;
-    const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR; // over batch*heads*n
-    const int part = tid % LPR;
-    const int64_t rows = (int64_t)p.total; // batch * heads * n here
-    if (row >= rows)
-        return;
-    const int t = (int)(row % p.n);
-    const int b = (int)(row / p.n / p.heads);
-    const int len = seq_len(p, b);
-    float acc = 0.0f;
-    if (t < len) {
-        const u32x4 a = *(const u32x4 *)(p.dout + row * D + part * 8);
-        const u32x4 o = *(const u32x4 *)(p.o + row * D + part * 8);
-        const bf16x8 av = __builtin_bit_cast(bf16x8, a), ov = __builtin_bit_cast(bf16x8, o);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            acc = fmaf((float)av[e], (float)ov[e], acc);
-    }
-#pragma unroll
-    for (int w = 1; w < LPR; w <<= 1)
-        acc += __shfl_xor(acc, w);
-    if (part == 0)
-        p.delta[row] = acc;
 }
 
 // ------------------------------------------------------------ shared parts
@@ -257,9 +225,12 @@ __global__ void __launch_bounds__(256) dq_kernel(BParams p)
     uint16_t *dq_row = p.dq + base + (size_t)qrow * D;
 
     if (i0 >= nb) { // a group of padding only
-        if (exists)
+        if (exists) {
             for (int c = lane; c < BLK * D / 8; c += 64)
                 *(u32x4 *)(p.dq + base + (size_t)i * BLK * D + (size_t)c * 8) = u32x4{0, 0, 0, 0};
+            if (half == 0)
+                p.delta[(size_t)bh * p.n + qrow] = 0.0f;
+        }
         return;
     }
     int lo_w = 1, hi_w = 0;
@@ -294,7 +265,23 @@ __global__ void __launch_bounds__(256) dq_kernel(BParams p)
         gf[s] = as_bf16x8(y);
     }
     const float lse2 = qvalid ? p.lse[(size_t)bh * p.n + qrow] * LOG2E : 0.0f;
-    const float Dt = qvalid ? p.delta[(size_t)bh * p.n + qrow] : 0.0f;
+    // D_t = sum_c dO_tc O_tc: this lane's half of the row (the dO fragments it
+    // holds) against the same elements of O, then the other half from lane +- 32;
+    // written for the key-stationary kernel, 0 on rows past the length
+    float Dt = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+        u32x4 z = u32x4{0, 0, 0, 0};
+        if (qvalid)
+            z = *(const u32x4 *)(p.o + base + (size_t)qrow * D + s * 16 + half * 8);
+        const bf16x8 ov = as_bf16x8(z);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            Dt = fmaf((float)gf[s][e], (float)ov[e], Dt);
+    }
+    Dt += __shfl_xor(Dt, 32);
+    if (exists && half == 0)
+        p.delta[(size_t)bh * p.n + qrow] = Dt;
 
 #pragma unroll
     for (int a = 0; a < NSTAGE - 1; ++a)
@@ -575,18 +562,9 @@ template <int D, bool CAUSAL>
 hipError_t launch_bwd_d(const BwdLaunch &a, BParams p)
 {
     constexpr int NS = 3;
-    // delta over every row of every (batch, head)
-    BParams pd = p;
-    const int64_t rows = (int64_t)a.batch * a.heads * a.n;
-    pd.total = (int32_t)rows;
-    constexpr int RPB = 256 / (D / 8);
-    const int64_t dblocks = (rows + RPB - 1) / RPB;
-    hipLaunchKernelGGL((delta_kernel<D>), dim3((unsigned)dblocks), dim3(256), 0, a.stream, pd);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
+    // dq also writes D (every row of every real block), which dkv reads
     hipLaunchKernelGGL((dq_kernel<D, NS, CAUSAL>), dim3(p.total), dim3(256), 0, a.stream, p);
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL((dkv_kernel<D, NS, CAUSAL>), dim3(p.total), dim3(256), 0, a.stream, p);
