@@ -178,8 +178,12 @@ template <int NMT>
 __device__ __forceinline__ void store_rowT(uint16_t *out_row, const f32x16 *acc, float mul, bool valid,
                                            int half)
 {
+    // lanes l and l + 32 hold the two 4-element halves of each 8-element run;
+    // one exchange gives each lane two whole runs, stored 16 bytes at a time
+    // (call with the whole wave active)
 #pragma unroll
     for (int m = 0; m < NMT; ++m) {
+        u32x2 pk4[4];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             f32x2 lo2 = {acc[m][4 * a] * mul, acc[m][4 * a + 1] * mul};
@@ -188,9 +192,19 @@ __device__ __forceinline__ void store_rowT(uint16_t *out_row, const f32x16 *acc,
                 lo2 = f32x2{0.0f, 0.0f};
                 hi2 = f32x2{0.0f, 0.0f};
             }
-            const u32x2 packed = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo2, bf16x2)),
-                                  __builtin_bit_cast(uint32_t, __builtin_convertvector(hi2, bf16x2))};
-            *(u32x2 *)(out_row + m * 32 + 8 * a + 4 * half) = packed;
+            pk4[a] = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(lo2, bf16x2)),
+                           __builtin_bit_cast(uint32_t, __builtin_convertvector(hi2, bf16x2))};
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const u32x2 mine = half ? pk4[2 * k + 1] : pk4[2 * k];
+            const u32x2 give = half ? pk4[2 * k] : pk4[2 * k + 1];
+            u32x2 got;
+            got[0] = (uint32_t)__shfl_xor((int)give[0], 32);
+            got[1] = (uint32_t)__shfl_xor((int)give[1], 32);
+            const u32x4 run = half ? u32x4{got[0], got[1], mine[0], mine[1]}
+                                   : u32x4{mine[0], mine[1], got[0], got[1]};
+            *(u32x4 *)(out_row + m * 32 + 8 * (2 * k + half)) = run;
         }
     }
 }
