@@ -219,3 +219,44 @@ def test_errors_write_nothing():
     torch.cuda.synchronize()
     assert torch.all(o == 3.0)
     plan.close()
+
+
+def test_large_tensors_64bit_offsets():
+    """2^31 elements per tensor (batch 1, 16 heads, 2^20 rows, head dim 128: 4 GiB
+    each in bf16), so row offsets past 2^31 bytes are exercised.  Inputs are
+    seeded normal draws made on the device (torch's generator); sampled query
+    blocks, the last ones of the last head among them, are checked against the
+    oracle on the slice of rows their band covers (the band of a query block
+    lies inside its own 2R + 1 blocks, so the slice gives the same keys)."""
+    heads, n, dd, R = 16, 1 << 20, 128, 8
+    say(f"[parity] large tensors 1 x {heads} x {n} x {dd} R{R}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    shape = (1, heads, n, dd)
+    q, k, v = (torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
+               .to(torch.bfloat16) for _ in range(3))
+    o = torch.full_like(q, float("nan"))
+    plan = bsl.Plan(head_dim=dd, heads=heads, radius=R, causal=False)
+    plan.forward(q, k, v, None, o=o)
+    torch.cuda.synchronize()
+    nblk = n // 32
+    picks = [(heads - 1, nblk - 1), (heads - 1, nblk - 2), (heads - 1, nblk - 9),
+             (heads - 1, 20000), (12, nblk - 1), (0, 0), (7, 5)]
+    worst = 0.0
+    for h, i in picks:
+        lo = max(0, i - R)
+        hi = min(nblk, i + R + 1)
+        rows = slice(lo * 32, hi * 32)
+        sub = [t[:, h:h + 1, rows].float().cpu().numpy() for t in (q, k, v)]
+        ln = np.array([(hi - lo) * 32], dtype=np.int32)
+        ref, _, _ = oracle.forward(sub[0], sub[1], sub[2], ln, 32, R, False)
+        r0 = (i - lo) * 32
+        want = ref[0, 0, r0:r0 + 32]
+        got = o[0, h, i * 32:(i + 1) * 32].float().cpu().numpy()
+        e = np.abs(got.astype(np.float64) - want)
+        worst = max(worst, float(e.max()))
+        assert np.all(np.isfinite(got)) and e.max() <= 2e-2 and e.mean() <= 2e-3, (h, i, e.max())
+    say(f"  {len(picks)} sampled blocks: max-abs {worst:.3e}")
+    plan.close()
+    del q, k, v, o
+    torch.cuda.empty_cache()
