@@ -54,9 +54,18 @@ def _declare(lib):
     lib.orc_backward_blocks_f64.argtypes = [i, i, i, i, i, i, i, ctypes.c_double, _i32p, _f32p,
                                             _f32p, _f32p, _f32p, ctypes.c_int64, _i32p, _f64p,
                                             _f64p, _f64p, i]
+    lib.orc_masks_w.argtypes = [i, i, i, i, i, i, _i32p, _i32p, _u32p]
+    lib.orc_forward_w_f64.argtypes = [i, i, i, i, i, i, i, i, ctypes.c_double, _i32p, _f32p,
+                                      _f32p, _f32p, _f64p, _f64p, _f64p, i]
+    lib.orc_forward_blocks_w_f64.argtypes = [i, i, i, i, i, i, i, i, ctypes.c_double, _i32p,
+                                             _f32p, _f32p, _f32p, ctypes.c_int64, _i32p, _f64p,
+                                             _f64p, _f64p, i]
+    lib.orc_forward_recurrence_w_f64.argtypes = [i, i, i, i, i, i, i, i, ctypes.c_double, _i32p,
+                                                 _f32p, _f32p, _f32p, _f64p]
     lib.orc_kmer_tokenize.argtypes = [i, ctypes.POINTER(ctypes.c_uint8),
                                       ctypes.POINTER(ctypes.c_int64), i, i, _i32p, _i32p]
-    for name in ("orc_kmer_tokenize", "orc_active_blocks", "orc_masks", "orc_forward_f64", "orc_forward_blocks_f64",
+    for name in ("orc_masks_w", "orc_forward_w_f64", "orc_forward_blocks_w_f64",
+                 "orc_forward_recurrence_w_f64", "orc_kmer_tokenize", "orc_active_blocks", "orc_masks", "orc_forward_f64", "orc_forward_blocks_f64",
                  "orc_forward_recurrence_f64", "orc_backward_f64", "orc_backward_blocks_f64"):
         getattr(lib, name).restype = i
     return lib
@@ -101,9 +110,21 @@ def _check(rc, name):
         raise OracleError(f"{name} failed with code {rc}")
 
 
-def active_blocks(batch, n, bsize, radius, causal, seqlens=None, lib=None):
-    """int32 [batch, n/bsize, 2R+1]: ascending visited key blocks, -1 padded."""
+def window_radius(window, bsize=32):
+    """The block radius a token window of ``window`` tokens reaches: ceil(W/B)."""
+    return -(-int(window) // int(bsize))
+
+
+def _radius(radius, window, bsize):
+    return radius if window is None else window_radius(window, bsize)
+
+
+def active_blocks(batch, n, bsize, radius, causal, seqlens=None, lib=None, window=None):
+    """int32 [batch, n/bsize, 2R+1]: ascending visited key blocks, -1 padded.
+    With a token window W, R = ceil(W/B) (every block of that band holds a
+    pair within W)."""
     lib = lib or load()
+    radius = _radius(radius, window, bsize)
     s = _lens(batch, n, seqlens)
     nblk = n // bsize if bsize > 0 else 0
     out = np.full((batch, nblk, max(2 * radius + 1, 1)), -7, dtype=np.int32)
@@ -112,17 +133,22 @@ def active_blocks(batch, n, bsize, radius, causal, seqlens=None, lib=None):
     return out
 
 
-def masks(batch, n, bsize, radius, causal, seqlens=None, active=None, lib=None):
+def masks(batch, n, bsize, radius, causal, seqlens=None, active=None, lib=None, window=None):
     """uint32 [batch, n/bsize, 2R+1, bsize]: word r bit c set iff key c of the
     slot's key block is kept for query row r of the query block."""
     lib = lib or load()
+    radius = _radius(radius, window, bsize)
     s = _lens(batch, n, seqlens)
     if active is None:
         active = active_blocks(batch, n, bsize, radius, causal, seqlens, lib=lib)
     active = np.ascontiguousarray(active, dtype=np.int32)
     out = np.zeros(active.shape + (bsize,), dtype=np.uint32)
-    _check(lib.orc_masks(batch, n, bsize, radius, int(causal), _ptr(s, _i32p),
-                         _ptr(active, _i32p), _ptr(out, _u32p)), "orc_masks")
+    if window is None:
+        _check(lib.orc_masks(batch, n, bsize, radius, int(causal), _ptr(s, _i32p),
+                             _ptr(active, _i32p), _ptr(out, _u32p)), "orc_masks")
+    else:
+        _check(lib.orc_masks_w(batch, n, bsize, radius, int(causal), int(window), _ptr(s, _i32p),
+                               _ptr(active, _i32p), _ptr(out, _u32p)), "orc_masks_w")
     return out
 
 
@@ -134,10 +160,13 @@ def _f32(a):
 
 
 def forward(q, k, v, seqlens=None, bsize=32, radius=1, causal=False, scale=0.0, nthreads=None,
-            lib=None):
+            lib=None, window=None):
     """Two-pass definition.  Returns (o [b,h,n,d], lse [b,h,n], psum [b,h,n])
-    in float64; psum is the sum of each row's normalised probabilities."""
+    in float64; psum is the sum of each row's normalised probabilities.
+    ``window`` (>= 0) selects the token window |t - s| <= W instead of the
+    block band."""
     lib = lib or load()
+    radius = _radius(radius, window, bsize)
     q, k, v = _f32(q), _f32(k), _f32(v)
     batch, heads, n, d = q.shape
     if k.shape != q.shape or v.shape != q.shape:
@@ -146,18 +175,27 @@ def forward(q, k, v, seqlens=None, bsize=32, radius=1, causal=False, scale=0.0, 
     o = np.empty((batch, heads, n, d), dtype=np.float64)
     lse = np.empty((batch, heads, n), dtype=np.float64)
     psum = np.empty((batch, heads, n), dtype=np.float64)
-    _check(lib.orc_forward_f64(batch, heads, n, d, bsize, radius, int(causal), float(scale),
-                               _ptr(s, _i32p), _ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p),
-                               _ptr(o, _f64p), _ptr(lse, _f64p), _ptr(psum, _f64p),
-                               nthreads or default_threads()), "orc_forward_f64")
+    if window is None:
+        _check(lib.orc_forward_f64(batch, heads, n, d, bsize, radius, int(causal), float(scale),
+                                   _ptr(s, _i32p), _ptr(q, _f32p), _ptr(k, _f32p),
+                                   _ptr(v, _f32p), _ptr(o, _f64p), _ptr(lse, _f64p),
+                                   _ptr(psum, _f64p), nthreads or default_threads()),
+               "orc_forward_f64")
+    else:
+        _check(lib.orc_forward_w_f64(batch, heads, n, d, bsize, radius, int(causal), int(window),
+                                     float(scale), _ptr(s, _i32p), _ptr(q, _f32p),
+                                     _ptr(k, _f32p), _ptr(v, _f32p), _ptr(o, _f64p),
+                                     _ptr(lse, _f64p), _ptr(psum, _f64p),
+                                     nthreads or default_threads()), "orc_forward_w_f64")
     return o, lse, psum
 
 
 def forward_blocks(q, k, v, sel, seqlens=None, bsize=32, radius=1, causal=False, scale=0.0,
-                   nthreads=None, lib=None):
+                   nthreads=None, lib=None, window=None):
     """Only the query blocks listed in ``sel`` (int array [m, 3] of (b, h, i)).
     Returns (o [m, bsize, d], lse [m, bsize], psum [m, bsize])."""
     lib = lib or load()
+    radius = _radius(radius, window, bsize)
     q, k, v = _f32(q), _f32(k), _f32(v)
     batch, heads, n, d = q.shape
     s = _lens(batch, n, seqlens)
@@ -166,27 +204,30 @@ def forward_blocks(q, k, v, sel, seqlens=None, bsize=32, radius=1, causal=False,
     o = np.empty((m, bsize, d), dtype=np.float64)
     lse = np.empty((m, bsize), dtype=np.float64)
     psum = np.empty((m, bsize), dtype=np.float64)
-    _check(lib.orc_forward_blocks_f64(batch, heads, n, d, bsize, radius, int(causal),
-                                      float(scale), _ptr(s, _i32p), _ptr(q, _f32p),
-                                      _ptr(k, _f32p), _ptr(v, _f32p), m, _ptr(sel, _i32p),
-                                      _ptr(o, _f64p), _ptr(lse, _f64p), _ptr(psum, _f64p),
-                                      nthreads or default_threads()), "orc_forward_blocks_f64")
+    _check(lib.orc_forward_blocks_w_f64(batch, heads, n, d, bsize, radius, int(causal),
+                                        -1 if window is None else int(window), float(scale),
+                                        _ptr(s, _i32p), _ptr(q, _f32p), _ptr(k, _f32p),
+                                        _ptr(v, _f32p), m, _ptr(sel, _i32p), _ptr(o, _f64p),
+                                        _ptr(lse, _f64p), _ptr(psum, _f64p),
+                                        nthreads or default_threads()), "orc_forward_blocks_w_f64")
     return o, lse, psum
 
 
 def forward_recurrence(q, k, v, seqlens=None, bsize=32, radius=1, causal=False, scale=0.0,
-                       lib=None):
+                       lib=None, window=None):
     """The page's running (m, d, O) recurrence, block by block, divided by d at
     the end.  Single threaded; meant for small inputs."""
     lib = lib or load()
+    radius = _radius(radius, window, bsize)
     q, k, v = _f32(q), _f32(k), _f32(v)
     batch, heads, n, d = q.shape
     s = _lens(batch, n, seqlens)
     o = np.empty((batch, heads, n, d), dtype=np.float64)
-    _check(lib.orc_forward_recurrence_f64(batch, heads, n, d, bsize, radius, int(causal),
-                                          float(scale), _ptr(s, _i32p), _ptr(q, _f32p),
-                                          _ptr(k, _f32p), _ptr(v, _f32p), _ptr(o, _f64p)),
-           "orc_forward_recurrence_f64")
+    _check(lib.orc_forward_recurrence_w_f64(batch, heads, n, d, bsize, radius, int(causal),
+                                            -1 if window is None else int(window), float(scale),
+                                            _ptr(s, _i32p), _ptr(q, _f32p), _ptr(k, _f32p),
+                                            _ptr(v, _f32p), _ptr(o, _f64p)),
+           "orc_forward_recurrence_w_f64")
     return o
 
 

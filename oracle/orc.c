@@ -55,6 +55,13 @@
  * padded to n_out tokens with PAD.  Special IDs: PAD = 4^k, MASK = 4^k + 1,
  * UNK = 4^k + 2, 4^k + 3 reserved (4^k + 4 entries: 4100 for k = 6).
  *
+ * The _w entry points take a token window W as well (section 2, item 3 of the
+ * page names a "local sliding neighborhood (W)" without defining it further;
+ * read plainly, key s is in reach of query t when |t - s| <= W): A(b,t) is then
+ *   { s : 0 <= s < len_b, |t - s| <= W, (causal => s <= t) },
+ * searched within the block band of radius ceil(W / B), the widest band such a
+ * window reaches.  W = -1 leaves the block band alone.
+ *
  * Inputs are float (the exact bf16- or fp32-rounded values a GPU consumes);
  * every product and sum is taken in double.  Q, K, V, O are [batch][heads][n][d]
  * contiguous.  All routines return 0 on success and a negative code on bad
@@ -87,6 +94,16 @@ static int check_shape(int batch, int n, int bsize, int radius, const int32_t *s
     return 0;
 }
 
+/* A token window must fit inside the block band that is searched for it. */
+static int check_window(int window, int radius, int bsize)
+{
+    if (window < -1)
+        return ORC_E_INVALID;
+    if (window >= 0 && radius < (window + bsize - 1) / bsize)
+        return ORC_E_INVALID;
+    return 0;
+}
+
 static int seq_len(const int32_t *seqlens, int b, int n) { return seqlens ? seqlens[b] : n; }
 
 /* Number of blocks that hold at least one real token: the padded length of a
@@ -106,12 +123,17 @@ static int block_in_band(int i, int j, int radius, int nb, int causal)
     return 1;
 }
 
-/* Is token pair (query t, key s) kept: the token-level set A(b,t) above. */
-static int pair_kept(int t, int s, int len, int bsize, int radius, int causal)
+/* Is token pair (query t, key s) kept: the token-level set A(b,t) above.  With
+ * a token window (window >= 0) the pair must also lie within window tokens of
+ * each other, |t - s| <= window; callers then pass radius = ceil(window / B),
+ * the widest block band such a window reaches. */
+static int pair_kept(int t, int s, int len, int bsize, int radius, int causal, int window)
 {
     if (t < 0 || t >= len || s < 0 || s >= len)
         return 0;
     if (abs(t / bsize - s / bsize) > radius)
+        return 0;
+    if (window >= 0 && abs(t - s) > window)
         return 0;
     if (causal && s > t)
         return 0;
@@ -150,10 +172,13 @@ int orc_active_blocks(int batch, int n, int bsize, int radius, int causal,
 /* masks[b][i][slot][r], bit c: for the slot-th active key block j of query block
  * i, key j*B + c is kept for query i*B + r.  Zero for unused slots and for query
  * rows past the sequence.  Needs B <= 32 (one 32-bit word per query row). */
-int orc_masks(int batch, int n, int bsize, int radius, int causal, const int32_t *seqlens,
-              const int32_t *active, uint32_t *masks)
+int orc_masks_w(int batch, int n, int bsize, int radius, int causal, int window,
+                const int32_t *seqlens, const int32_t *active, uint32_t *masks)
 {
     int rc = check_shape(batch, n, bsize, radius, seqlens);
+    if (rc)
+        return rc;
+    rc = check_window(window, radius, bsize);
     if (rc)
         return rc;
     if (bsize > 32)
@@ -172,7 +197,8 @@ int orc_masks(int batch, int n, int bsize, int radius, int causal, const int32_t
                     uint32_t w = 0;
                     if (j >= 0)
                         for (int c = 0; c < bsize; ++c)
-                            if (pair_kept(i * bsize + r, j * bsize + c, len, bsize, radius, causal))
+                            if (pair_kept(i * bsize + r, j * bsize + c, len, bsize, radius, causal,
+                                          window))
                                 w |= (uint32_t)1 << c;
                     words[r] = w;
                 }
@@ -189,6 +215,7 @@ typedef struct {
     double scale;
     const int32_t *seqlens;
     const float *q, *k, *v;
+    int window; /* < 0: the block band alone */
 } problem;
 
 /* One query row t of (b, h): the plain definition above.  o_row gets d values;
@@ -222,7 +249,7 @@ static void row_definition(const problem *p, int b, int h, int t, double *sbuf,
     int cnt = 0;
     double m = -INFINITY;
     for (int s = s_lo; s < s_hi; ++s) {
-        if (!pair_kept(t, s, len, p->bsize, p->radius, p->causal))
+        if (!pair_kept(t, s, len, p->bsize, p->radius, p->causal, p->window))
             continue;
         const float *ks = p->k + (base + s) * d;
         double dot = 0.0;
@@ -356,6 +383,9 @@ static int check_problem(const problem *p)
     int rc = check_shape(p->batch, p->n, p->bsize, p->radius, p->seqlens);
     if (rc)
         return rc;
+    rc = check_window(p->window, p->radius, p->bsize);
+    if (rc)
+        return rc;
     if (p->heads < 0 || p->d < 1)
         return ORC_E_INVALID;
     if (!(p->scale > 0.0) || !isfinite(p->scale))
@@ -368,11 +398,13 @@ static double pick_scale(double scale, int d) { return scale > 0.0 ? scale : 1.0
 
 /* Full forward: o [batch][heads][n][d], lse and psum [batch][heads][n] (either
  * may be NULL). */
-int orc_forward_f64(int batch, int heads, int n, int d, int bsize, int radius, int causal,
-                    double scale, const int32_t *seqlens, const float *q, const float *k,
-                    const float *v, double *o, double *lse, double *psum, int nthreads)
+int orc_forward_w_f64(int batch, int heads, int n, int d, int bsize, int radius, int causal,
+                      int window, double scale, const int32_t *seqlens, const float *q,
+                      const float *k, const float *v, double *o, double *lse, double *psum,
+                      int nthreads)
 {
-    problem p = {batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v};
+    problem p = {batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v,
+                 window};
     int rc = check_problem(&p);
     if (rc)
         return rc;
@@ -394,12 +426,14 @@ int orc_forward_f64(int batch, int heads, int n, int d, int bsize, int radius, i
 
 /* Selected query blocks only: sel[w] = (b, h, i).  o [nsel][bsize][d], lse and
  * psum [nsel][bsize].  The inputs are the full-size tensors. */
-int orc_forward_blocks_f64(int batch, int heads, int n, int d, int bsize, int radius, int causal,
-                           double scale, const int32_t *seqlens, const float *q, const float *k,
-                           const float *v, int64_t nsel, const int32_t *sel, double *o,
-                           double *lse, double *psum, int nthreads)
+int orc_forward_blocks_w_f64(int batch, int heads, int n, int d, int bsize, int radius,
+                             int causal, int window, double scale, const int32_t *seqlens,
+                             const float *q, const float *k, const float *v, int64_t nsel,
+                             const int32_t *sel, double *o, double *lse, double *psum,
+                             int nthreads)
 {
-    problem p = {batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v};
+    problem p = {batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v,
+                 window};
     int rc = check_problem(&p);
     if (rc)
         return rc;
@@ -434,11 +468,12 @@ int orc_forward_blocks_f64(int batch, int heads, int n, int d, int bsize, int ra
  *   O_new = O_old * exp(m_old - m_new) + sum_c exp(S_ic - m_new) V_c
  * per query row, starting from m = -inf, d = 0, O = 0, with masked scores set to
  * -inf; after the last block O / d is the output.  Single threaded. */
-int orc_forward_recurrence_f64(int batch, int heads, int n, int d, int bsize, int radius,
-                               int causal, double scale, const int32_t *seqlens, const float *q,
-                               const float *k, const float *v, double *o)
+int orc_forward_recurrence_w_f64(int batch, int heads, int n, int d, int bsize, int radius,
+                                 int causal, int window, double scale, const int32_t *seqlens,
+                                 const float *q, const float *k, const float *v, double *o)
 {
-    problem p = {batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v};
+    problem p = {batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v,
+                 window};
     int rc = check_problem(&p);
     if (rc)
         return rc;
@@ -477,7 +512,7 @@ int orc_forward_recurrence_f64(int batch, int heads, int n, int d, int bsize, in
                     for (int c = 0; c < bsize; ++c) {
                         const int s = j * bsize + c;
                         double sc = -INFINITY;
-                        if (pair_kept(t, s, len, bsize, radius, causal)) {
+                        if (pair_kept(t, s, len, bsize, radius, causal, window)) {
                             double dot = 0.0;
                             for (int e = 0; e < d; ++e)
                                 dot += (double)q[(base + t) * d + e] * (double)k[(base + s) * d + e];
@@ -516,6 +551,38 @@ int orc_forward_recurrence_f64(int batch, int heads, int n, int d, int bsize, in
     return 0;
 }
 
+/* The entry points without a token window: the block band alone. */
+int orc_masks(int batch, int n, int bsize, int radius, int causal, const int32_t *seqlens,
+              const int32_t *active, uint32_t *masks)
+{
+    return orc_masks_w(batch, n, bsize, radius, causal, -1, seqlens, active, masks);
+}
+
+int orc_forward_f64(int batch, int heads, int n, int d, int bsize, int radius, int causal,
+                    double scale, const int32_t *seqlens, const float *q, const float *k,
+                    const float *v, double *o, double *lse, double *psum, int nthreads)
+{
+    return orc_forward_w_f64(batch, heads, n, d, bsize, radius, causal, -1, scale, seqlens, q, k, v,
+                             o, lse, psum, nthreads);
+}
+
+int orc_forward_blocks_f64(int batch, int heads, int n, int d, int bsize, int radius, int causal,
+                           double scale, const int32_t *seqlens, const float *q, const float *k,
+                           const float *v, int64_t nsel, const int32_t *sel, double *o,
+                           double *lse, double *psum, int nthreads)
+{
+    return orc_forward_blocks_w_f64(batch, heads, n, d, bsize, radius, causal, -1, scale, seqlens,
+                                    q, k, v, nsel, sel, o, lse, psum, nthreads);
+}
+
+int orc_forward_recurrence_f64(int batch, int heads, int n, int d, int bsize, int radius,
+                               int causal, double scale, const int32_t *seqlens, const float *q,
+                               const float *k, const float *v, double *o)
+{
+    return orc_forward_recurrence_w_f64(batch, heads, n, d, bsize, radius, causal, -1, scale,
+                                        seqlens, q, k, v, o);
+}
+
 /* ------------------------------------------------------------ backward pass */
 
 typedef struct {
@@ -551,7 +618,7 @@ static void row_backward(const bproblem *bp, int b, int h, int t, double *sbuf, 
         if (s_hi > len)
             s_hi = len;
         for (int s = s_lo; s < s_hi; ++s)
-            if (pair_kept(t, s, len, p->bsize, p->radius, p->causal))
+            if (pair_kept(t, s, len, p->bsize, p->radius, p->causal, p->window))
                 ++cnt;
         double l = 0.0;
         for (int e = 0; e < cnt; ++e)
@@ -685,7 +752,8 @@ int orc_backward_f64(int batch, int heads, int n, int d, int bsize, int radius, 
                      const float *v, const float *dout, double *dq, double *dk, double *dv,
                      int nthreads)
 {
-    bproblem bp = {{batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v},
+    bproblem bp = {{batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v,
+                    -1},
                    dout};
     int rc = check_problem(&bp.fw);
     if (rc)
@@ -715,7 +783,8 @@ int orc_backward_blocks_f64(int batch, int heads, int n, int d, int bsize, int r
                             const float *v, const float *dout, int64_t nsel, const int32_t *sel,
                             double *dq, double *dk, double *dv, int nthreads)
 {
-    bproblem bp = {{batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v},
+    bproblem bp = {{batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v,
+                    -1},
                    dout};
     int rc = check_problem(&bp.fw);
     if (rc)

@@ -7,17 +7,22 @@ textbook exp / sum over a masked row.  Tiny inputs only.
 import numpy as np
 
 
-def token_mask(n, length, bsize, radius, causal):
-    """bool [n, n]: entry (t, s) kept."""
+def token_mask(n, length, bsize, radius, causal, window=None):
+    """bool [n, n]: entry (t, s) kept.  With ``window`` the band is the token
+    window |t - s| <= window instead of the block band."""
     t = np.arange(n)[:, None]
     s = np.arange(n)[None, :]
-    keep = (t < length) & (s < length) & (np.abs(t // bsize - s // bsize) <= radius)
+    if window is None:
+        near = np.abs(t // bsize - s // bsize) <= radius
+    else:
+        near = np.abs(t - s) <= window
+    keep = (t < length) & (s < length) & near
     if causal:
         keep &= s <= t
     return keep
 
 
-def dense_reference(q, k, v, seqlens, bsize, radius, causal, scale=None):
+def dense_reference(q, k, v, seqlens, bsize, radius, causal, scale=None, window=None):
     """float64 (o, lse) from a dense masked softmax."""
     q = q.astype(np.float64)
     k = k.astype(np.float64)
@@ -28,7 +33,7 @@ def dense_reference(q, k, v, seqlens, bsize, radius, causal, scale=None):
     lse = np.full((batch, heads, n), -np.inf)
     for b in range(batch):
         L = int(seqlens[b]) if seqlens is not None else n
-        keep = token_mask(n, L, bsize, radius, causal)
+        keep = token_mask(n, L, bsize, radius, causal, window)
         for h in range(heads):
             qq = np.nan_to_num(q[b, h], nan=0.0)
             kk = np.nan_to_num(k[b, h], nan=0.0)

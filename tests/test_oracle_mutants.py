@@ -274,3 +274,65 @@ def test_kmer_mutant_is_caught(name):
         lib_path = obuild.build(out=os.path.join(tmp, "liborc_mutant.so"), src=path)
         lib = oracle.load(lib_path)
         assert _kmer_battery(lib) != [], f"mutant {name} slipped through every pin"
+
+
+# ------------------------------------------------------------ token window
+
+WINDOW_MUTANTS = {
+    "window_off_by_one": ("if (window >= 0 && abs(t - s) > window)",
+                          "if (window >= 0 && abs(t - s) >= window)"),
+    "window_ignored": ("if (window >= 0 && abs(t - s) > window)",
+                       "if (window >= 1 << 30 && abs(t - s) > window)"),
+    "window_one_sided": ("if (window >= 0 && abs(t - s) > window)",
+                         "if (window >= 0 && t - s > window)"),
+}
+
+
+def _window_battery(lib):
+    failed = []
+    rng = np.random.default_rng(7)
+    for bsize, window, causal, lens in [(32, 5, False, [96, 70]), (8, 12, True, [96, 41]),
+                                        (4, 0, False, [32, 17])]:
+        n = 96 if bsize != 4 else 32
+        lens = np.array(lens, dtype=np.int32)
+        q, k, v = [(rng.standard_normal((2, 1, n, 8))).astype(np.float32) for _ in range(3)]
+        try:
+            o, _, _ = oracle.forward(q, k, v, lens, bsize, 0, causal, lib=lib, window=window)
+            ro, _ = dense_reference(q, k, v, lens, bsize, 0, causal, window=window)
+            if not np.max(np.abs(o - ro)) <= 1e-12:
+                failed.append("brute_force")
+            act = oracle.active_blocks(2, n, bsize, 0, causal, lens, lib=lib, window=window)
+            msk = oracle.masks(2, n, bsize, 0, causal, lens, act, lib=lib, window=window)
+            for b in range(2):
+                keep = token_mask(n, int(lens[b]), bsize, 0, causal, window)
+                for i in range(n // bsize):
+                    for slot, j in enumerate(act[b, i]):
+                        if j < 0:
+                            continue
+                        blk = keep[i * bsize:(i + 1) * bsize, j * bsize:(j + 1) * bsize]
+                        words = [sum(1 << c for c in range(bsize) if blk[r, c])
+                                 for r in range(bsize)]
+                        if list(msk[b, i, slot]) != words:
+                            failed.append("masks")
+        except oracle.OracleError:
+            failed.append("error")
+    return sorted(set(failed))
+
+
+def test_unmodified_oracle_passes_window_battery():
+    assert _window_battery(oracle.load()) == []
+
+
+@pytest.mark.parametrize("name", sorted(WINDOW_MUTANTS))
+def test_window_mutant_is_caught(name):
+    old, new = WINDOW_MUTANTS[name]
+    with open(obuild.SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "orc_mutant.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        lib_path = obuild.build(out=os.path.join(tmp, "liborc_mutant.so"), src=path)
+        lib = oracle.load(lib_path)
+        assert _window_battery(lib) != [], f"mutant {name} slipped through every pin"
