@@ -20,7 +20,9 @@ steps between two device synchronisations.  Prints one JSON line:
 
 The default workload is the 1.3B-shape long-context case: batch 1, 16 heads,
 131072-row buffer holding a 130000-token sequence, head dim 128, radius 8.
-``--secondary`` also times the million-token case in the same run.
+``--secondary`` also times the million-token case in the same run;
+``--window W`` also times the chosen workload with a token window of W tokens
+(|t - s| <= W) in place of the block band.
 """
 import argparse
 import hashlib
@@ -129,10 +131,11 @@ def pack_device(x, lens):
     return torch.cat([x[b, :, :int(L)].transpose(0, 1) for b, L in enumerate(lens)]).contiguous()
 
 
-def time_workload(key, steps, warmup, cold=False, log=print, layout="padded"):
+def time_workload(key, steps, warmup, cold=False, log=print, layout="padded", window=0):
     """Times bsl_forward on the workload (layout "padded": [batch][heads][n][d])
     or bsl_forward_varlen on the same sequences packed ("packed":
-    [tokens][heads][d], no padding between sequences)."""
+    [tokens][heads][d], no padding between sequences); window >= 1 replaces the
+    block band with a token window of that many tokens."""
     import torch
     from block_sparse_local_amd import bsl, inputs, workload
 
@@ -140,9 +143,10 @@ def time_workload(key, steps, warmup, cold=False, log=print, layout="padded"):
     d = inputs.make(key, 42)
     w = d["workload"]
     lens = d["seqlens"]
-    log(f"[bench] {key} inputs drawn in {time.time() - t0:.1f}s: {w.describe()} ({layout})")
+    log(f"[bench] {key} inputs drawn in {time.time() - t0:.1f}s: {w.describe()} ({layout}"
+        f"{f', token window {window}' if window else ''})")
     q, k, v = (to_device(d[x], w.dtype) for x in ("q", "k", "v"))
-    plan = bsl.Plan(w.d, w.heads, w.radius, w.causal, w.dtype)
+    plan = bsl.Plan(w.d, w.heads, w.radius, w.causal, w.dtype, window=window)
     if layout == "packed":
         q, k, v = (pack_device(x, lens) for x in (q, k, v))
         cu_host, max_len, _ = bsl.bsl_varlen_offsets(lens)
@@ -157,7 +161,7 @@ def time_workload(key, steps, warmup, cold=False, log=print, layout="padded"):
             plan.forward(q, k, v, sl, o=o, stream=stream)
     o = torch.empty_like(q)
     buffer_bytes = 4 * q.numel() * q.element_size()
-    acc = workload.account(lens, w.heads, w.d, w.radius, w.causal, w.dtype)
+    acc = workload.account(lens, w.heads, w.d, w.radius, w.causal, w.dtype, window)
     stream = torch.cuda.current_stream()
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if cold else None
 
@@ -182,7 +186,7 @@ def time_workload(key, steps, warmup, cold=False, log=print, layout="padded"):
     del q, k, v, o, flush
     torch.cuda.empty_cache()
     return dict(key=key, w=w, d=d, acc=acc, wall=wall, per_launch=per_launch, steps=steps,
-                layout=layout, buffer_bytes=buffer_bytes)
+                layout=layout, buffer_bytes=buffer_bytes, window=window)
 
 
 def time_backward(key, steps, warmup, log=print):
@@ -274,9 +278,10 @@ def cpu_baseline(r, target_flops=1.0e12, log=print):
                 sel.append((b, h, int(i)))
     sel = np.array(sel, dtype=np.int32)
     threads = min(16, oracle.default_threads())
+    window = r.get("window", 0)
     t0 = time.perf_counter()
     oracle.forward_blocks(d["q"], d["k"], d["v"], sel, lens, 32, w.radius, w.causal,
-                          nthreads=threads)
+                          nthreads=threads, window=window if window > 0 else None)
     dt = time.perf_counter() - t0
     # useful work of exactly the sampled query rows
     flops = 0.0
@@ -289,10 +294,7 @@ def cpu_baseline(r, target_flops=1.0e12, log=print):
         for i in np.unique(rows[:, 2]):
             hcount = int((rows[:, 2] == i).sum())
             t = np.arange(i * 32, min(L, i * 32 + 32))
-            lo = np.maximum(0, (t // 32 - w.radius) * 32)
-            hi = np.minimum(L, (t // 32 + w.radius + 1) * 32)
-            if w.causal:
-                hi = np.minimum(hi, t + 1)
+            lo, hi = workload.key_range(t, L, w.radius, w.causal, window)
             flops += 4.0 * w.d * float((hi - lo).sum()) * hcount
             tokens += len(t) * hcount
     log(f"[bench] oracle: {len(sel)} (sequence, head, query block) units in {dt:.1f}s "
@@ -438,6 +440,9 @@ def main():
     ap.add_argument("--kmer", action="store_true",
                     help="also time the fused k-mer tokenizer (bsl_kmer_tokenize)")
     ap.add_argument("--kmer-workload", default="k1", choices=["k1", "k2"])
+    ap.add_argument("--window", type=int, default=0,
+                    help="also time the workload with a token window of this many tokens "
+                         "(bsl_desc.window) in place of the block band")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 1 GiB device copies (for counter calibration)")
     args = ap.parse_args()
@@ -509,6 +514,20 @@ def main():
             f"({roofv['frac'] * 100:.1f}% of {roofv['bound']} peak); buffers "
             f"{rv['buffer_bytes'] / 2**20:.1f} MiB vs {padded_bytes / 2**20:.1f} MiB padded")
         del rv
+    if args.window > 0:
+        rw = time_workload(args.workload, args.steps, args.warmup, args.cold, log,
+                           window=args.window)
+        tw, roofw, extraw = summarize(rw, None)
+        line["window"] = {"window": args.window, "band_radius": -(-args.window // 32),
+                          "ms_per_step": tw * 1e3, "value": extraw["useful_tflops"],
+                          "unit": "TFLOP/s", "tokens_per_s": extraw["tokens_per_s"],
+                          "roofline": roofw, "detail": extraw}
+        if not args.no_cpu_baseline:
+            line["window"]["cpu_baseline"] = cpu_baseline(rw, log=log)
+        log(f"[bench] {args.workload} token window {args.window}: {tw * 1e3:.3f} ms/step, "
+            f"{extraw['useful_tflops']:.1f} useful TFLOP/s ({roofw['frac'] * 100:.1f}% of "
+            f"{roofw['bound']} peak)")
+        del rw
     if args.secondary and args.workload != "c5":
         r5 = time_workload("c5", args.steps, args.warmup, args.cold, log)
         t5, roof5, extra5 = summarize(r5, stored_traffic("c5"))

@@ -38,11 +38,12 @@ class BslError(RuntimeError):
 class BslDesc(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("radius", ctypes.c_int32),
-                ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("window", ctypes.c_int32)]
 
     def __init__(self, head_dim=64, heads=1, radius=1, causal=False, dtype=BSL_BF16, scale=0.0,
-                 block_size=32):
-        super().__init__(head_dim, heads, block_size, radius, int(causal), dtype, scale)
+                 block_size=32, window=0):
+        super().__init__(head_dim, heads, block_size, radius, int(causal), dtype, scale, window)
 
 
 _lib = None
@@ -229,11 +230,17 @@ def bsl_version():
 class Plan:
     """A plan plus shape/dtype checks for torch tensors on the current GPU."""
 
-    def __init__(self, head_dim, heads, radius, causal=False, dtype="bf16", scale=0.0):
+    def __init__(self, head_dim, heads, radius, causal=False, dtype="bf16", scale=0.0, window=0):
         self.head_dim, self.heads, self.radius, self.causal = head_dim, heads, radius, causal
-        self.dtype = dtype
+        self.dtype, self.window = dtype, window
         code = {"bf16": BSL_BF16, "f32": BSL_F32}[dtype]
-        self.handle = bsl_create(BslDesc(head_dim, heads, radius, causal, code, scale))
+        self.handle = bsl_create(BslDesc(head_dim, heads, radius, causal, code, scale,
+                                         window=window))
+
+    @property
+    def band_radius(self):
+        """The block radius the kernels sweep: R, or ceil(W / 32) with a token window."""
+        return -(-self.window // 32) if self.window > 0 else self.radius
 
     def close(self):
         if self.handle is not None:
@@ -277,7 +284,7 @@ class Plan:
             o = torch.empty_like(q)
         self._check_tensors(q, k, v, o, seqlens, lse)
         batch, n = q.shape[0], q.shape[2]
-        w = 2 * self.radius + 1
+        w = 2 * self.band_radius + 1
         active = torch.empty((batch, n // 32, w), dtype=torch.int32, device=q.device)
         masks = torch.empty((batch, n // 32, w, 32), dtype=torch.int32, device=q.device)
         bsl_forward_traced(self.handle, batch, n, q, k, v, o, seqlens, lse, active, masks, stream)

@@ -37,6 +37,13 @@ bsl_status fail(bsl_status s, const char *fmt, ...)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The block band the kernels sweep: R itself, or with a token window W the
+// ceil(W / 32) blocks on either side that hold every key within W tokens.
+int32_t band_radius(const bsl_desc &d)
+{
+    return d.window > 0 ? (d.window + d.block_size - 1) / d.block_size : d.radius;
+}
+
 bsl_status run(const bsl_plan *plan, int32_t batch, int32_t n, const void *q, const void *k,
                const void *v, void *o, const int32_t *seqlens, float *lse, int32_t *active,
                uint32_t *masks, void *stream, bool traced)
@@ -95,7 +102,8 @@ bsl_status run(const bsl_plan *plan, int32_t batch, int32_t n, const void *q, co
     a.n = n;
     a.tokens = 0;
     a.head_dim = d.head_dim;
-    a.radius = d.radius;
+    a.radius = band_radius(d);
+    a.window = d.window;
     a.causal = d.causal != 0;
     a.scale = plan->scale;
     a.stream = (hipStream_t)stream;
@@ -163,7 +171,8 @@ bsl_status run_varlen(const bsl_plan *plan, int32_t batch, int32_t tokens, int32
     a.n = max_seqlen;
     a.tokens = tokens;
     a.head_dim = d.head_dim;
-    a.radius = d.radius;
+    a.radius = band_radius(d);
+    a.window = d.window;
     a.causal = d.causal != 0;
     a.scale = plan->scale;
     a.stream = (hipStream_t)stream;
@@ -183,6 +192,8 @@ bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
     const bsl_desc &d = plan->desc;
     if (d.dtype != BSL_BF16)
         return fail(BSL_E_UNSUPPORTED, "the backward pass is built for bf16 plans only");
+    if (d.window != 0)
+        return fail(BSL_E_UNSUPPORTED, "the backward pass supports the block band only (window 0)");
     if (d.head_dim != 64 && d.head_dim != 128)
         return fail(BSL_E_UNSUPPORTED, "the backward pass supports head_dim 64 and 128 (got %d)",
                     d.head_dim);
@@ -284,8 +295,12 @@ bsl_status bsl_create(const bsl_desc *desc, bsl_plan **plan)
         return fail(BSL_E_UNSUPPORTED, "head_dim must be 32, 64 or 128 (got %d)", d.head_dim);
     if (d.dtype != BSL_BF16 && d.dtype != BSL_F32)
         return fail(BSL_E_UNSUPPORTED, "unknown dtype %d", d.dtype);
+    if (d.window < 0)
+        return fail(BSL_E_INVALID, "window must be >= 0 (got %d)", d.window);
     if (d.radius > (1 << 24))
         return fail(BSL_E_UNSUPPORTED, "radius %d is too large", d.radius);
+    if (d.window > (1 << 29))
+        return fail(BSL_E_UNSUPPORTED, "window %d is too large", d.window);
 
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess)

@@ -97,6 +97,7 @@ struct Params {
     // n: padded buffer length, or the longest sequence the grid covers (packed)
     int32_t heads, n, nblk, ngroups, radius, total;
     int32_t tokens; // packed layout: rows in the buffer
+    int32_t window; // 0: the block band; >= 1: keys within this many tokens
     float c;        // scale * log2(e)
 };
 
@@ -319,7 +320,11 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             oacc[m][r] = 0.0f;
-    float m_used = -INFINITY; // reference maximum (log2 units)
+    // reference maximum (log2 units).  Finite, so that a block whose keys all
+    // lie outside a row's token window (all scores -inf) gives exp2(-inf) = 0
+    // rather than exp2(-inf + inf); the first real score replaces it with
+    // alpha = exp2(-1e30 - m) = 0, as -inf would.
+    float m_used = -1.0e30f;
     float lsum = 0.0f;        // this lane's share of the denominator
 
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -371,14 +376,20 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
             }
 
-            // padding and causal masks: only the last real block and the diagonal
-            const bool need_mask = pad_block || (CAUSAL && j == i);
+            // padding and causal masks: only the last real block and the
+            // diagonal; a token window also cuts every block whose farthest
+            // query-key pair, 32 |j - i| + 31 tokens apart, lies outside it
+            const int dj = j > i ? j - i : i - j;
+            const bool need_mask = pad_block || (CAUSAL && j == i) ||
+                                   (p.window > 0 && dj * BLK + BLK - 1 > p.window);
             uint32_t part = 0;
             if (need_mask) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = j * BLK + acc_row(r, half);
-                    const bool keep = key < len && (!CAUSAL || key <= qrow);
+                    const int dist = qrow > key ? qrow - key : key - qrow;
+                    const bool keep = key < len && (!CAUSAL || key <= qrow) &&
+                                      (p.window <= 0 || dist <= p.window);
                     s[r] = keep ? s[r] : -INFINITY;
                     if (TRACE)
                         part |= (keep ? 1u : 0u) << acc_row(r, half);
@@ -564,6 +575,7 @@ hipError_t launch_fwd_bf16(const Launch &a)
     p.nblk = (a.n + BLK - 1) / BLK;
     p.ngroups = (p.nblk + MQ - 1) / MQ;
     p.radius = a.radius;
+    p.window = a.window;
     p.total = a.batch * a.heads * p.ngroups;
     p.c = a.scale * LOG2E;
     switch (a.head_dim) {

@@ -34,6 +34,7 @@ struct Params {
     // n: padded buffer length, or the longest sequence the grid covers (packed)
     int32_t heads, n, nblk, radius, total;
     int32_t tokens; // packed layout: rows in the buffer
+    int32_t window; // 0: the block band; >= 1: keys within this many tokens
     float c;        // scale * log2(e)
 };
 
@@ -94,7 +95,10 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(Params p)
         qv[e] = tvalid ? p.q[base + (size_t)t * RS + e * 8 + sub] : 0.0f;
         ov[e] = 0.0f;
     }
-    float m = -INFINITY, l = 0.0f;
+    // running maximum: finite, so that a block whose keys all lie outside the
+    // row's token window leaves alpha = exp2(0) and weights exp2(-inf) = 0
+    // instead of NaN; the first real score gives alpha = exp2(-1e30 - m) = 0
+    float m = -1.0e30f, l = 0.0f;
 
     for (int j = lo; j <= hi; ++j) {
         __syncthreads();
@@ -122,7 +126,8 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(Params p)
             part += __shfl_xor(part, 2);
             part += __shfl_xor(part, 4);
             const int s = j * BLK + c;
-            const bool keep = s < len && (!CAUSAL || s <= t);
+            const int dist = t > s ? t - s : s - t;
+            const bool keep = s < len && (!CAUSAL || s <= t) && (p.window <= 0 || dist <= p.window);
             sc[c] = keep ? part * p.c : -INFINITY;
             word |= (keep ? 1u : 0u) << c;
             bmax = fmaxf(bmax, sc[c]);
@@ -135,7 +140,7 @@ __global__ void __launch_bounds__(256) fwd_f32_kernel(Params p)
                 p.active[slot] = j;
         }
         const float mn = fmaxf(m, bmax);
-        const float alpha = __builtin_amdgcn_exp2f(m - mn); // 0 on the first block
+        const float alpha = __builtin_amdgcn_exp2f(m - mn); // 0 at the first kept key
         float add = 0.0f;
 #pragma unroll
         for (int e = 0; e < E; ++e)
@@ -209,6 +214,7 @@ hipError_t launch_fwd_f32(const Launch &a)
     p.tokens = a.tokens;
     p.nblk = (a.n + BLK - 1) / BLK;
     p.radius = a.radius;
+    p.window = a.window;
     p.total = a.batch * a.heads * p.nblk;
     p.c = a.scale * LOG2E;
     switch (a.head_dim) {

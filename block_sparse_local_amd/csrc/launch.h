@@ -19,6 +19,7 @@ struct Launch {
     uint32_t *masks;
     int32_t batch, heads, n, head_dim, radius;
     int32_t tokens;
+    int32_t window; // 0: block band; >= 1: token window (radius = ceil(window / 32))
     bool causal;
     float scale; // already resolved (> 0)
     hipStream_t stream;

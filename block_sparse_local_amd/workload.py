@@ -5,6 +5,9 @@ Used for reporting only (bench.py); nothing here runs on the compute path.
 useful pairs   kept (query t, key s) pairs summed over sequences and heads: for
                row t of block i = t // 32 the keys run from max(0, (i-R)*32) to
                min(len, (i+R+1)*32) (exclusive), or to t + 1 when causal.
+               With a token window W the keys run from max(0, t-W) to
+               min(len, t+W+1) (or t + 1 when causal), and the kernel's band
+               is R = ceil(W/32).
 useful FLOP    4 * d per useful pair (2d for Q.K, 2d for P.V); exp and the
                final division are not counted.
 block pairs    (query block, key block) pairs the kernel computes, each a
@@ -26,20 +29,36 @@ MI355X_FP32_VECTOR_FLOPS = 157.3e12
 MI355X_HBM_BYTES = 8.0e12
 
 
-def useful_pairs_per_head(lens, radius, causal):
-    total = 0
-    for L in np.asarray(lens, dtype=np.int64):
-        t = np.arange(int(L), dtype=np.int64)
+def band_radius(radius, window=0):
+    """The block radius swept: R, or ceil(W/32) for a token window W >= 1."""
+    return -(-int(window) // BLOCK) if window > 0 else radius
+
+
+def key_range(t, L, radius, causal, window=0):
+    """Kept keys [lo, hi) of query rows t (int64 array) of a length-L sequence."""
+    if window > 0:
+        lo = np.maximum(0, t - window)
+        hi = np.minimum(int(L), t + window + 1)
+    else:
         i = t // BLOCK
         lo = np.maximum(0, (i - radius) * BLOCK)
         hi = np.minimum(int(L), (i + radius + 1) * BLOCK)
-        if causal:
-            hi = np.minimum(hi, t + 1)
+    if causal:
+        hi = np.minimum(hi, t + 1)
+    return lo, hi
+
+
+def useful_pairs_per_head(lens, radius, causal, window=0):
+    total = 0
+    for L in np.asarray(lens, dtype=np.int64):
+        t = np.arange(int(L), dtype=np.int64)
+        lo, hi = key_range(t, L, radius, causal, window)
         total += int((hi - lo).sum())
     return total
 
 
-def block_pairs_per_head(lens, radius, causal):
+def block_pairs_per_head(lens, radius, causal, window=0):
+    radius = band_radius(radius, window)
     total = 0
     for L in lens:
         nb = -(-int(L) // BLOCK)
@@ -52,10 +71,10 @@ def block_pairs_per_head(lens, radius, causal):
     return total
 
 
-def account(lens, heads, d, radius, causal, dtype="bf16"):
+def account(lens, heads, d, radius, causal, dtype="bf16", window=0):
     esz = 2 if dtype == "bf16" else 4
-    up = useful_pairs_per_head(lens, radius, causal) * heads
-    bp = block_pairs_per_head(lens, radius, causal) * heads
+    up = useful_pairs_per_head(lens, radius, causal, window) * heads
+    bp = block_pairs_per_head(lens, radius, causal, window) * heads
     tokens = int(np.sum(lens))
     flops = 4.0 * d * up
     computed = 4.0 * d * BLOCK * BLOCK * bp

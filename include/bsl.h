@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define BSL_VERSION 10300 /* major * 10000 + minor * 100 + patch */
+#define BSL_VERSION 10400 /* major * 10000 + minor * 100 + patch */
 
 typedef enum bsl_status {
     BSL_OK = 0,
@@ -68,15 +68,24 @@ typedef struct bsl_desc {
     int32_t causal;     /* 0 or 1: 1 also drops keys s > t */
     int32_t dtype;      /* a bsl_dtype */
     float scale;        /* > 0: score scale; <= 0: 1 / sqrt(head_dim) */
+    int32_t window;     /* 0: the block band of radius R (the page's rule).
+                           W >= 1: a token window instead, the plain reading
+                           of the local neighbourhood W of section 2, item 3:
+                           key s is scored for query t when |t - s| <= W,
+                           over the blocks within ceil(W/32) of the query
+                           block.  radius is then not used (it must still be
+                           >= 0).  Forward and packed forward only: a plan
+                           with a window gets BSL_E_UNSUPPORTED from
+                           bsl_backward. */
 } bsl_desc;
 
 typedef struct bsl_plan bsl_plan;
 
 /* Validate *desc against the current HIP device and make a plan for it.
  * BSL_E_INVALID: desc or plan NULL, heads < 1, radius < 0, causal not 0/1,
- *   non-finite scale.
+ *   non-finite scale, window < 0.
  * BSL_E_UNSUPPORTED: head_dim not 32/64/128, block_size != 32, unknown dtype,
- *   or the current device is not gfx950.
+ *   window > 2^29, radius > 2^24, or the current device is not gfx950.
  * BSL_E_DEVICE: the device could not be queried.
  * On success *plan is set; release it with bsl_destroy. */
 bsl_status bsl_create(const bsl_desc *desc, bsl_plan **plan);
@@ -99,7 +108,8 @@ bsl_status bsl_forward(const bsl_plan *plan, int32_t batch, int32_t n, const voi
                        const void *k, const void *v, void *o, const int32_t *seqlens,
                        float *lse, void *stream);
 
-/* bsl_forward, plus a record of what the kernel did, for verification:
+/* bsl_forward, plus a record of what the kernel did, for verification.  Below,
+ * R is the plan's radius, or ceil(window / 32) for a plan with a token window.
  *   active  device int32[batch][n/32][2R+1]: for query block i of sequence b,
  *           the key blocks the kernel visited, ascending, then -1 in the unused
  *           slots (all -1 for blocks that hold only padding).
@@ -179,9 +189,10 @@ bsl_status bsl_varlen_offsets(int32_t batch, const int32_t *lengths, int32_t *cu
  *            call overwrites it with D (0 on padded rows).  The library
  *            allocates nothing.
  * All tensors 16-byte aligned.  dq, dk, dv and delta must not overlap each
- * other or any input.  Returns BSL_E_UNSUPPORTED for an fp32 plan or head_dim
- * 32, BSL_E_INVALID for the argument errors bsl_forward rejects, a NULL
- * pointer, misalignment or overlap, and BSL_E_DEVICE if a launch fails.
+ * other or any input.  Returns BSL_E_UNSUPPORTED for an fp32 plan, a plan with
+ * a token window, or head_dim 32, BSL_E_INVALID for the argument errors
+ * bsl_forward rejects, a NULL pointer, misalignment or overlap, and
+ * BSL_E_DEVICE if a launch fails.
  * Nothing is written when an argument error is returned. */
 bsl_status bsl_backward(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
                         const void *k, const void *v, const void *o, const void *dout,

@@ -56,8 +56,8 @@
  * UNK = 4^k + 2, 4^k + 3 reserved (4^k + 4 entries: 4100 for k = 6).
  *
  * The _w entry points take a token window W as well (section 2, item 3 of the
- * page names a "local sliding neighborhood (W)" without defining it further;
- * read plainly, key s is in reach of query t when |t - s| <= W): A(b,t) is then
+ * page bounds the receptive field by a local neighbourhood W and says no more
+ * of it; read plainly, key s is in reach of query t when |t - s| <= W): A(b,t) is then
  *   { s : 0 <= s < len_b, |t - s| <= W, (causal => s <= t) },
  * searched within the block band of radius ceil(W / B), the widest band such a
  * window reaches.  W = -1 leaves the block band alone.

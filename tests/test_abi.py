@@ -29,6 +29,13 @@ def _declared():
     return sorted(set(re.findall(r"\b(bsl_[a-z_]+)\s*\(", text)))
 
 
+def test_desc_layout_matches_header():
+    """bsl_desc is seven int32/float fields then window: 32 bytes, window last."""
+    assert ctypes.sizeof(bsl.BslDesc) == 32
+    assert bsl.BslDesc.window.offset == 28
+    assert bsl.BslDesc().window == 0
+
+
 def test_header_and_binding_agree():
     assert _declared() == sorted(bsl.EXPORTS)
 
@@ -68,6 +75,8 @@ def _create_status(lib, **kw):
     (dict(head_dim=48), bsl.BSL_E_UNSUPPORTED),
     (dict(head_dim=256), bsl.BSL_E_UNSUPPORTED),
     (dict(dtype=7), bsl.BSL_E_UNSUPPORTED),
+    (dict(window=-1), bsl.BSL_E_INVALID),
+    (dict(window=(1 << 29) + 1), bsl.BSL_E_UNSUPPORTED),
 ])
 def test_create_rejects_bad_descriptors_before_device_use(lib, kw, status):
     st, plan = _create_status(lib, **kw)

@@ -95,6 +95,19 @@ def test_account_matches_the_oracle(key):
     assert acc["tokens"] == int(np.sum(lens))
 
 
+@pytest.mark.parametrize("window,causal", [(1, False), (33, True), (100, False), (256, True)])
+def test_account_window_matches_the_oracle(window, causal):
+    lens = np.array([1000, 0, 33, 517], np.int32)
+    n = 1024
+    act = oracle.active_blocks(len(lens), n, 32, 0, causal, lens, window=window)
+    msk = oracle.masks(len(lens), n, 32, 0, causal, lens, act, window=window)
+    bits = int(np.unpackbits(msk.astype("<u4").view(np.uint8)).sum())
+    acc = workload.account(lens, 3, 64, 0, causal, "bf16", window=window)
+    assert acc["useful_pairs"] == bits * 3
+    assert acc["block_pairs"] == int((act >= 0).sum()) * 3
+    assert acc["alg_bytes"] == 4.0 * int(lens.sum()) * 3 * 64 * 2
+
+
 def test_account_bound_and_peaks():
     # bf16 at this shape is memory bound; fp32 is priced against the vector ALUs
     a = workload.account([4096], 16, 128, 8, False, "bf16")

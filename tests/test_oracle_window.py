@@ -1,7 +1,7 @@
 """Pins for the oracle's token-window variant (CPU only).
 
-The NucleoByte page names a "local sliding neighborhood (W)" (section 2, item
-3) but gives no rule for it beyond the block band; read plainly, key s is in
+The NucleoByte page bounds attention to a local neighbourhood W (section 2,
+item 3) but gives no rule for it beyond the block band; read plainly, key s is in
 reach of query t when |t - s| <= W.  The oracle's window mode is pinned by:
   * W = 0: every row attends to itself alone, so O = V row by row and lse is
     the row's own score (closed form);
