@@ -510,6 +510,9 @@ def main():
                           "buffer_bytes": rv["buffer_bytes"],
                           "padded_buffer_bytes": padded_bytes,
                           "padded_ms_per_step": t_step * 1e3}
+        if not args.no_cpu_baseline:
+            # the oracle has one layout: the same sequences, the same operation
+            line["varlen"]["cpu_baseline"] = cpu_baseline(rv, log=log)
         log(f"[bench] {args.workload} packed: {tv * 1e3:.3f} ms/step "
             f"({roofv['frac'] * 100:.1f}% of {roofv['bound']} peak); buffers "
             f"{rv['buffer_bytes'] / 2**20:.1f} MiB vs {padded_bytes / 2**20:.1f} MiB padded")
