@@ -25,7 +25,7 @@ BSL_BF16, BSL_F32 = 0, 1
 # every function include/bsl.h declares
 EXPORTS = ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_forward_varlen",
            "bsl_varlen_offsets", "bsl_backward", "bsl_kmer_tokenize", "bsl_kmer_ceiling",
-           "bsl_destroy", "bsl_status_string",
+           "bsl_check_seqlens", "bsl_check_cu_seqlens", "bsl_destroy", "bsl_status_string",
            "bsl_last_error", "bsl_version")
 
 
@@ -75,6 +75,8 @@ def load(path=LIB_PATH):
     lib.bsl_backward.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.bsl_kmer_tokenize.argtypes = [i32, vp, ctypes.c_int64, vp, i32, i32, vp, vp, vp]
     lib.bsl_kmer_ceiling.argtypes = [i32, ctypes.POINTER(ctypes.c_int64), i32, ctypes.POINTER(i32)]
+    lib.bsl_check_seqlens.argtypes = [i32, i32, vp, vp, vp]
+    lib.bsl_check_cu_seqlens.argtypes = [i32, i32, vp, vp, vp]
     lib.bsl_destroy.argtypes = [vp]
     lib.bsl_status_string.argtypes = [ctypes.c_int]
     lib.bsl_status_string.restype = ctypes.c_char_p
@@ -84,7 +86,7 @@ def load(path=LIB_PATH):
     lib.bsl_version.restype = i32
     for name in ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_forward_varlen",
                  "bsl_varlen_offsets", "bsl_backward", "bsl_kmer_tokenize", "bsl_kmer_ceiling",
-                 "bsl_destroy"):
+                 "bsl_check_seqlens", "bsl_check_cu_seqlens", "bsl_destroy"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -163,6 +165,33 @@ def bsl_backward(plan, batch, n, q, k, v, o, dout, lse, seqlens, dq, dk, dv, del
 def bsl_kmer_tokenize(batch, bases, nbytes, starts, k, n_out, ids, ntok=None, stream=None):
     _check(load().bsl_kmer_tokenize(batch, _ptr(bases), nbytes, _ptr(starts), k, n_out, _ptr(ids),
                                     _ptr(ntok), _stream(stream)))
+
+
+def bsl_check_seqlens(batch, n, seqlens, result, stream=None):
+    _check(load().bsl_check_seqlens(batch, n, _ptr(seqlens), _ptr(result), _stream(stream)))
+
+
+def bsl_check_cu_seqlens(batch, tokens, cu_seqlens, result, stream=None):
+    _check(load().bsl_check_cu_seqlens(batch, tokens, _ptr(cu_seqlens), _ptr(result),
+                                       _stream(stream)))
+
+
+def check_seqlens(seqlens, n):
+    """Device int32 lengths -> (bad entries, first bad index or -1); waits for the result."""
+    import torch
+    res = torch.empty(2, dtype=torch.int32, device=seqlens.device)
+    bsl_check_seqlens(seqlens.numel(), n, seqlens, res)
+    bad, first = res.tolist()
+    return bad, first
+
+
+def check_cu_seqlens(cu_seqlens, tokens):
+    """Device int32 offsets [batch + 1] -> (bad entries, first bad index or -1)."""
+    import torch
+    res = torch.empty(2, dtype=torch.int32, device=cu_seqlens.device)
+    bsl_check_cu_seqlens(cu_seqlens.numel() - 1, tokens, cu_seqlens, res)
+    bad, first = res.tolist()
+    return bad, first
 
 
 def bsl_kmer_ceiling(starts, k=6):

@@ -453,6 +453,35 @@ bsl_status bsl_kmer_tokenize(int32_t batch, const uint8_t *bases, int64_t nbytes
     return BSL_OK;
 }
 
+static bsl_status check_common(int32_t batch, int32_t limit, const int32_t *v, int32_t *result,
+                               void *stream, int mode)
+{
+    const char *what = mode == 0 ? "seqlens" : "cu_seqlens";
+    if (batch < 0 || limit < 0)
+        return fail(BSL_E_INVALID, "batch (%d) and the limit (%d) must be >= 0", batch, limit);
+    if ((!v && (mode == 1 || batch > 0)) || !result)
+        return fail(BSL_E_INVALID, "%s and result must be non-NULL device pointers", what);
+    const size_t entries = (size_t)batch + (mode == 0 ? 0 : 1);
+    if (v && overlaps(v, entries * 4, result, 8))
+        return fail(BSL_E_INVALID, "result overlaps %s", what);
+    const hipError_t e = bsl::launch_check(v, batch, limit, mode, result, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(BSL_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    return BSL_OK;
+}
+
+bsl_status bsl_check_seqlens(int32_t batch, int32_t n, const int32_t *seqlens, int32_t *result,
+                             void *stream)
+{
+    return check_common(batch, n, seqlens, result, stream, 0);
+}
+
+bsl_status bsl_check_cu_seqlens(int32_t batch, int32_t tokens, const int32_t *cu_seqlens,
+                                int32_t *result, void *stream)
+{
+    return check_common(batch, tokens, cu_seqlens, result, stream, 1);
+}
+
 bsl_status bsl_kmer_ceiling(int32_t batch, const int64_t *starts, int32_t k, int32_t *n_out)
 {
     if (batch < 0)

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define BSL_VERSION 10400 /* major * 10000 + minor * 100 + patch */
+#define BSL_VERSION 10500 /* major * 10000 + minor * 100 + patch */
 
 typedef enum bsl_status {
     BSL_OK = 0,
@@ -253,6 +253,28 @@ bsl_status bsl_kmer_tokenize(int32_t batch, const uint8_t *bases, int64_t nbytes
  * work.  BSL_E_INVALID for batch < 0, a NULL pointer, k outside 1 .. 12,
  * decreasing or negative offsets, or a result past 2^31 - 1. */
 bsl_status bsl_kmer_ceiling(int32_t batch, const int64_t *starts, int32_t k, int32_t *n_out);
+
+/* Debug validators for the device-side lengths and offsets the forward reads.
+ * The forward itself clamps them (a bad value cannot cause an out-of-bounds
+ * access, but it changes which rows are attended); these report them instead,
+ * without a host round trip.  One small kernel is enqueued on `stream`; it
+ * writes result[0] = the number of bad entries and result[1] = the index of
+ * the first one, or -1 when all are valid.
+ *   bsl_check_seqlens:    seqlens device int32[batch]; entry b is bad when
+ *                         outside [0, n] (n as passed to bsl_forward).
+ *   bsl_check_cu_seqlens: cu_seqlens device int32[batch + 1]; entry 0 is bad
+ *                         when not 0, entry b > 0 when below entry b - 1 or
+ *                         above tokens (as passed to bsl_forward_varlen).
+ *   result                device int32[2], written in full; must not overlap
+ *                         the checked array.
+ * batch == 0 still writes {0, -1} (cu_seqlens then holds one entry).
+ * BSL_E_INVALID for batch < 0, n or tokens < 0, a NULL pointer, or overlap;
+ * BSL_E_DEVICE if the launch fails.  Nothing is written on an argument error.
+ * The library allocates nothing and does not synchronise. */
+bsl_status bsl_check_seqlens(int32_t batch, int32_t n, const int32_t *seqlens, int32_t *result,
+                             void *stream);
+bsl_status bsl_check_cu_seqlens(int32_t batch, int32_t tokens, const int32_t *cu_seqlens,
+                                int32_t *result, void *stream);
 
 /* Release a plan.  NULL is accepted and ignored.  Do not call while work
  * enqueued with the plan is being launched from another thread. */

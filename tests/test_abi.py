@@ -188,3 +188,22 @@ def test_kmer_argument_errors_before_any_launch(lib):
     assert lib.bsl_kmer_tokenize(2, 4096, 100, 8192, 6, 8, 4100, None, None) == 1
     # batch 0 is a no-op
     assert lib.bsl_kmer_tokenize(0, None, 0, None, 6, 8, None, None, None) == 0
+
+
+def test_check_validators_reject_bad_arguments_before_any_launch(lib):
+    """The length/offset validators validate their arguments on the host, so
+    these errors need no GPU; nothing is launched."""
+    fake = ctypes.c_void_p(0x10000)
+    other = ctypes.c_void_p(0x20000)
+    assert lib.bsl_check_seqlens(-1, 32, fake, other, None) == bsl.BSL_E_INVALID
+    assert lib.bsl_check_seqlens(2, -1, fake, other, None) == bsl.BSL_E_INVALID
+    assert lib.bsl_check_seqlens(2, 32, None, other, None) == bsl.BSL_E_INVALID
+    assert lib.bsl_check_seqlens(2, 32, fake, None, None) == bsl.BSL_E_INVALID
+    # the result may not overlap the checked array
+    assert lib.bsl_check_seqlens(4, 32, fake, ctypes.c_void_p(0x10008), None) == bsl.BSL_E_INVALID
+    assert lib.bsl_check_cu_seqlens(-1, 10, fake, other, None) == bsl.BSL_E_INVALID
+    assert lib.bsl_check_cu_seqlens(1, -5, fake, other, None) == bsl.BSL_E_INVALID
+    # offsets always hold batch + 1 entries, so NULL is an error even for batch 0
+    assert lib.bsl_check_cu_seqlens(0, 10, None, other, None) == bsl.BSL_E_INVALID
+    assert lib.bsl_check_cu_seqlens(2, 10, fake, ctypes.c_void_p(0x10004), None) == bsl.BSL_E_INVALID
+    assert "overlaps" in bsl.bsl_last_error()
