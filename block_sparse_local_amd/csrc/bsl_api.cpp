@@ -3,6 +3,7 @@
 // synchronisation, nothing thrown across the interface.
 #include "bsl.h"
 
+#include "check.h"
 #include "launch.h"
 
 #include <hip/hip_runtime.h>

@@ -9,7 +9,7 @@
 // two-int32 device result.  Lengths follow the NucleoByte project page,
 // section 2, item 2 ("Dynamic Ceiling Hardware Alignment"): each sequence
 // fits its batch's padded length n.
-#include "launch.h"
+#include "check.h"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>

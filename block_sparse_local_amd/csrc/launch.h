@@ -66,10 +66,4 @@ struct KmerLaunch {
 int kmer_tiles(int32_t n_out);
 hipError_t launch_kmer(const KmerLaunch &a);
 
-// Length / offset validator (check.hip): mode 0 checks count lengths against
-// [0, limit], mode 1 checks count + 1 offsets (first 0, non-decreasing, at
-// most limit); writes {bad entries, first bad index or -1} to out[2].
-hipError_t launch_check(const int32_t *v, int32_t count, int32_t limit, int mode, int32_t *out,
-                        hipStream_t stream);
-
 } // namespace bsl
