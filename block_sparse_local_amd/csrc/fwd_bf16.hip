@@ -37,7 +37,9 @@
 //  * l is summed from the same bf16-rounded probabilities the PV product uses.
 //  * Padded keys of the last block are masked by select (never by a multiply),
 //    and their V rows are zeroed in LDS once the block has landed, so NaN
-//    padding cannot leak.
+//    padding cannot leak.  A token window W (section 2, item 3, read as
+//    |t - s| <= W) sweeps the ceil(W/32) blocks on either side and masks, by
+//    the same select, only the blocks whose farthest pair lies beyond W.
 //  * Workgroup ids are remapped so that each XCD (its own L2) works through a
 //    contiguous run of query groups: neighbouring groups share K/V halo blocks.
 //  * Vector memory instructions are what the texture addresser spends its time

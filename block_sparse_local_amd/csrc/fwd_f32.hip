@@ -11,7 +11,9 @@
 // query row t / 8 and the head dimensions e * 8 + t % 8 of it; the eight threads
 // of a row reduce their partial dot products with three xor shuffles.  Each
 // active K/V block is staged in LDS, and the row state (m, l, O slice) is updated
-// once per block, as the page's recurrence is written.
+// once per block, as the page's recurrence is written.  With a token window W
+// (section 2, item 3, read as |t - s| <= W) the band is the ceil(W/32) blocks on
+// either side and the window joins the per-key mask.
 #include "launch.h"
 
 #include <math.h>
