@@ -272,6 +272,25 @@ bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
     return BSL_OK;
 }
 
+// Argument checks and launch shared by the two validators (mode 0: lengths,
+// mode 1: offsets).
+bsl_status check_common(int32_t batch, int32_t limit, const int32_t *v, int32_t *result,
+                        void *stream, int mode)
+{
+    const char *what = mode == 0 ? "seqlens" : "cu_seqlens";
+    if (batch < 0 || limit < 0)
+        return fail(BSL_E_INVALID, "batch (%d) and the limit (%d) must be >= 0", batch, limit);
+    if ((!v && (mode == 1 || batch > 0)) || !result)
+        return fail(BSL_E_INVALID, "%s and result must be non-NULL device pointers", what);
+    const size_t entries = (size_t)batch + (mode == 0 ? 0 : 1);
+    if (v && overlaps(v, entries * 4, result, 8))
+        return fail(BSL_E_INVALID, "result overlaps %s", what);
+    const hipError_t e = bsl::launch_check(v, batch, limit, mode, result, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(BSL_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    return BSL_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -449,23 +468,6 @@ bsl_status bsl_kmer_tokenize(int32_t batch, const uint8_t *bases, int64_t nbytes
         a.n_out = 0;
     }
     const hipError_t e = bsl::launch_kmer(a);
-    if (e != hipSuccess)
-        return fail(BSL_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
-    return BSL_OK;
-}
-
-static bsl_status check_common(int32_t batch, int32_t limit, const int32_t *v, int32_t *result,
-                               void *stream, int mode)
-{
-    const char *what = mode == 0 ? "seqlens" : "cu_seqlens";
-    if (batch < 0 || limit < 0)
-        return fail(BSL_E_INVALID, "batch (%d) and the limit (%d) must be >= 0", batch, limit);
-    if ((!v && (mode == 1 || batch > 0)) || !result)
-        return fail(BSL_E_INVALID, "%s and result must be non-NULL device pointers", what);
-    const size_t entries = (size_t)batch + (mode == 0 ? 0 : 1);
-    if (v && overlaps(v, entries * 4, result, 8))
-        return fail(BSL_E_INVALID, "result overlaps %s", what);
-    const hipError_t e = bsl::launch_check(v, batch, limit, mode, result, (hipStream_t)stream);
     if (e != hipSuccess)
         return fail(BSL_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return BSL_OK;
