@@ -156,3 +156,19 @@ def test_window_plan_backward_is_unsupported():
     torch.cuda.synchronize()
     assert torch.isnan(dq).all()   # nothing written
     plan.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_extreme_window_and_radius(dtype):
+    """The largest window (2^29, band 2^24 blocks) and the largest radius (2^24)
+    are accepted and reduce to the band that covers the buffer: same bits."""
+    nblk = 6
+    lens = [nblk * 32, 77]
+    d = _case(5, dtype, 64, nblk, lens)
+    kw = dict(head_dim=64, heads=2, causal=False, dtype=dtype)
+    say(f"[window] extreme window / radius ({dtype})")
+    ref = run(dict(kw, radius=nblk), d, with_lse=True)
+    for extra in (dict(radius=0, window=1 << 29), dict(radius=1 << 24)):
+        got = run(dict(kw, **extra), d, with_lse=True)
+        assert np.array_equal(got["o"].view(np.uint32), ref["o"].view(np.uint32)), extra
+        assert np.array_equal(got["lse"].view(np.uint32), ref["lse"].view(np.uint32)), extra
