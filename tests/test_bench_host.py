@@ -155,3 +155,4 @@ def test_account_backward():
     l4, _ = inputs.lengths(c4, 42)
     b4 = workload.account_backward(l4, c4.heads, c4.d, c4.radius, c4.causal, c4.dtype)
     assert b4["bound"] == "mfma" and b4["t_mfma"] > b4["t_hbm"]
+
