@@ -6,7 +6,7 @@ nucleotide corpora the pages train on (GENCODE transcripts), which are not
 needed to exercise the attention forward: Q, K, V are activations, replaced here
 by normal draws of the shapes and scales below.
 
-Recipe (also in DESIGN.md):
+Recipe:
   * every [n, d] slice (tensor t in {Q=0, K=1, V=2, dO=3}, sequence b, head h; dO
     is the output gradient the backward pass takes) has its
     own PCG64 stream ``numpy.random.default_rng([seed, cfg, t, b, h])``, so the

@@ -6,7 +6,7 @@ The GPU forward runs first and its bf16 O and lse feed the backward, as in
 training.  Padded rows of Q, K, V and dO hold NaN and every output starts as
 NaN, so a kernel that reads padding or skips an element fails.
 
-Tolerance (derivation in the design doc): the kernels round P and dS to bf16
+Tolerance: the kernels round P and dS to bf16
 (relative 2^-9) before the products and take D from the bf16 O, so each
 gradient element carries a relative error of a few 2^-9 of the terms it sums.
 The bar is max-abs <= 2e-2 * s and mean-abs <= 2e-3 * s, with s the root mean
