@@ -43,6 +43,24 @@ def test_workload_full_oracle(key):
     _check_trace(res, w, d)
 
 
+@pytest.mark.parametrize("seed", [43, 44, 45, 46])
+@pytest.mark.parametrize("key", ["c1", "c2", "c3"])
+def test_workload_seed_sweep(key, seed):
+    """The correctness sweep over further seeds (new values and, for the mRNA
+    batch, new ragged lengths), whole outputs against the oracle and the
+    trace bit-exact."""
+    say(f"[parity] {key} seed {seed}")
+    d = inputs.make(key, seed, poison=True)
+    w = d["workload"]
+    res = run(_plan_kw(w), d, traced=True, with_lse=True)
+    o, lse, _ = oracle.forward(d["q"], d["k"], d["v"], d["seqlens"], 32, w.radius, w.causal)
+    check_rows(res["o"], o, d["seqlens"], w.dtype, f"{key} seed {seed}")
+    for b, L in enumerate(d["seqlens"]):
+        assert np.all(np.isneginf(res["lse"][b, :, L:]))
+        assert np.max(np.abs(res["lse"][b, :, :L] - lse[b, :, :L])) <= LSE_TOL[w.dtype]
+    _check_trace(res, w, d)
+
+
 def _sample_c4(nblk, nb, rng):
     pick = {0, 1, 2, nb - 3, nb - 2, nb - 1, nb, nblk - 1}
     pick |= set(int(x) for x in rng.choice(nblk, 56, replace=False))
