@@ -86,6 +86,8 @@ def code_text(src):
     return _scan(bare, False, lambda ws: "\n" if "\n" in ws else " ").strip()
 
 
+BWD_SOURCES = ["block_sparse_local_amd/csrc/bwd_bf16.hip", "block_sparse_local_amd/csrc/cdna4.h",
+               "block_sparse_local_amd/csrc/launch.h"]
 KMER_SOURCES = ["block_sparse_local_amd/csrc/kmer.hip", "block_sparse_local_amd/csrc/launch.h"]
 
 
@@ -505,7 +507,7 @@ def main():
     del r
     if args.varlen:
         rv = time_workload(args.workload, args.steps, args.warmup, args.cold, log, "packed")
-        tv, roofv, extrav = summarize(rv, None)
+        tv, roofv, extrav = summarize(rv, stored_traffic(args.workload, "fwd_bf16_packed"))
         line["varlen"] = {"layout": "packed [tokens][heads][head_dim], offsets cu_seqlens",
                           "ms_per_step": tv * 1e3, "value": extrav["useful_tflops"],
                           "unit": "TFLOP/s", "tokens_per_s": extrav["tokens_per_s"],
@@ -523,7 +525,7 @@ def main():
     if args.window > 0:
         rw = time_workload(args.workload, args.steps, args.warmup, args.cold, log,
                            window=args.window)
-        tw, roofw, extraw = summarize(rw, None)
+        tw, roofw, extraw = summarize(rw, stored_traffic(f"{args.workload}_window{args.window}"))
         line["window"] = {"window": args.window, "band_radius": -(-args.window // 32),
                           "ms_per_step": tw * 1e3, "value": extraw["useful_tflops"],
                           "unit": "TFLOP/s", "tokens_per_s": extraw["tokens_per_s"],
@@ -545,7 +547,7 @@ def main():
             f"({roof5['frac'] * 100:.1f}%)")
     if args.backward and r_w_dtype == "bf16":
         rb = time_backward(args.workload, args.steps, args.warmup, log)
-        tb, roofb, extrab = summarize(rb, None)
+        tb, roofb, extrab = summarize(rb, stored_traffic(args.workload, "bwd_bf16", BWD_SOURCES))
         line["backward"] = {"ms_per_step": tb * 1e3, "value": extrab["useful_tflops"],
                             "unit": "TFLOP/s", "tokens_per_s": extrab["tokens_per_s"],
                             "roofline": roofb, "detail": extrab}
