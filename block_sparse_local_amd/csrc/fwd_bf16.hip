@@ -184,11 +184,16 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
     const int g = xcd_remap((int)blockIdx.x, p.total);
     // Padded layout: a head's query groups are consecutive, so a run of groups
     // streams through one contiguous [n][D] slice.  Packed layout: a token's
-    // heads sit side by side in memory, so the heads of one query group are
-    // consecutive and a run of groups reads whole token rows.
-    const int grp = VARLEN ? (g / p.heads) % p.ngroups : g % p.ngroups;
-    const int b = VARLEN ? g / p.heads / p.ngroups : g / p.ngroups / p.heads;
-    const int h = VARLEN ? g % p.heads : (g / p.ngroups) % p.heads;
+    // heads sit side by side in memory.  With pieces of 128 bytes per head and
+    // row (D 64 or less) the heads of one query group run consecutively, so a
+    // run of groups reads whole token rows; with 256-byte pieces each piece is
+    // already two full lines, and head-major order (as padded) keeps the
+    // groups that share a head's halo blocks side by side, in the same L2 at
+    // the same time.
+    constexpr bool HEADS_FASTEST = VARLEN && D * 2 < 256;
+    const int grp = HEADS_FASTEST ? (g / p.heads) % p.ngroups : g % p.ngroups;
+    const int b = HEADS_FASTEST ? g / p.heads / p.ngroups : g / p.ngroups / p.heads;
+    const int h = HEADS_FASTEST ? g % p.heads : (g / p.ngroups) % p.heads;
     const int bh = b * p.heads + h;
     const Seq<D, VARLEN> sq(p, b, h, bh);
     const int len = sq.len;
