@@ -194,6 +194,28 @@ def time_workload(key, steps, warmup, cold=False, log=print, layout="padded", wi
                 layout=layout, buffer_bytes=buffer_bytes, window=window)
 
 
+def copy_bandwidth(reps=10):
+    """Achievable HBM rate on this GPU, for context beside the 8 TB/s peak: a
+    1 GiB device-to-device copy, bytes read + written over its mean time."""
+    import torch
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(reps):
+        b.copy_(a)
+    ev[1].record()
+    torch.cuda.synchronize()
+    sec = ev[0].elapsed_time(ev[1]) * 1e-3 / reps
+    nbytes = 2 * a.numel() * a.element_size()
+    del a, b
+    torch.cuda.empty_cache()
+    return {"value": nbytes / sec / 1e9, "unit": "GB/s",
+            "what": "1 GiB device-to-device copy (torch), read + written bytes over time"}
+
+
 def time_backward(key, steps, warmup, log=print):
     """The backward pass (bsl_backward) on the workload's inputs and a seeded
     output gradient, after one forward that supplies O and lse."""
@@ -495,6 +517,7 @@ def main():
         "tokens_per_s": extra["tokens_per_s"],
         "roofline": roof,
         "detail": extra,
+        "copy_bandwidth": copy_bandwidth(),
     }
     if args.cold:
         line["timing"] = "cold: 1 GiB overwritten between steps"
