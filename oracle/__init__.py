@@ -62,11 +62,17 @@ def _declare(lib):
                                              _f64p, _f64p, i]
     lib.orc_forward_recurrence_w_f64.argtypes = [i, i, i, i, i, i, i, i, ctypes.c_double, _i32p,
                                                  _f32p, _f32p, _f32p, _f64p]
+    lib.orc_backward_w_f64.argtypes = [i, i, i, i, i, i, i, i, ctypes.c_double, _i32p, _f32p,
+                                       _f32p, _f32p, _f32p, _f64p, _f64p, _f64p, i]
+    lib.orc_backward_blocks_w_f64.argtypes = [i, i, i, i, i, i, i, i, ctypes.c_double, _i32p,
+                                              _f32p, _f32p, _f32p, _f32p, ctypes.c_int64, _i32p,
+                                              _f64p, _f64p, _f64p, i]
     lib.orc_kmer_tokenize.argtypes = [i, ctypes.POINTER(ctypes.c_uint8),
                                       ctypes.POINTER(ctypes.c_int64), i, i, _i32p, _i32p]
     for name in ("orc_masks_w", "orc_forward_w_f64", "orc_forward_blocks_w_f64",
                  "orc_forward_recurrence_w_f64", "orc_kmer_tokenize", "orc_active_blocks", "orc_masks", "orc_forward_f64", "orc_forward_blocks_f64",
-                 "orc_forward_recurrence_f64", "orc_backward_f64", "orc_backward_blocks_f64"):
+                 "orc_forward_recurrence_f64", "orc_backward_f64", "orc_backward_blocks_f64",
+                 "orc_backward_w_f64", "orc_backward_blocks_w_f64"):
         getattr(lib, name).restype = i
     return lib
 
@@ -232,10 +238,12 @@ def forward_recurrence(q, k, v, seqlens=None, bsize=32, radius=1, causal=False, 
 
 
 def backward(q, k, v, dout, seqlens=None, bsize=32, radius=1, causal=False, scale=0.0,
-             nthreads=None, lib=None):
+             nthreads=None, lib=None, window=None):
     """Gradients of the forward with respect to q, k, v for the output gradient
-    ``dout`` (float32 [b,h,n,d]).  Returns (dq, dk, dv), float64 [b,h,n,d]."""
+    ``dout`` (float32 [b,h,n,d]).  Returns (dq, dk, dv), float64 [b,h,n,d].
+    ``window`` (>= 0): the gradients of the token-window forward."""
     lib = lib or load()
+    radius = _radius(radius, window, bsize)
     q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
     batch, heads, n, d = q.shape
     if k.shape != q.shape or v.shape != q.shape or dout.shape != q.shape:
@@ -244,19 +252,21 @@ def backward(q, k, v, dout, seqlens=None, bsize=32, radius=1, causal=False, scal
     dq = np.empty((batch, heads, n, d), dtype=np.float64)
     dk = np.empty_like(dq)
     dv = np.empty_like(dq)
-    _check(lib.orc_backward_f64(batch, heads, n, d, bsize, radius, int(causal), float(scale),
-                                _ptr(s, _i32p), _ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p),
-                                _ptr(dout, _f32p), _ptr(dq, _f64p), _ptr(dk, _f64p),
-                                _ptr(dv, _f64p), nthreads or default_threads()),
-           "orc_backward_f64")
+    _check(lib.orc_backward_w_f64(batch, heads, n, d, bsize, radius, int(causal),
+                                  -1 if window is None else int(window), float(scale),
+                                  _ptr(s, _i32p), _ptr(q, _f32p), _ptr(k, _f32p), _ptr(v, _f32p),
+                                  _ptr(dout, _f32p), _ptr(dq, _f64p), _ptr(dk, _f64p),
+                                  _ptr(dv, _f64p), nthreads or default_threads()),
+           "orc_backward_w_f64")
     return dq, dk, dv
 
 
 def backward_blocks(q, k, v, dout, sel, seqlens=None, bsize=32, radius=1, causal=False,
-                    scale=0.0, nthreads=None, lib=None):
+                    scale=0.0, nthreads=None, lib=None, window=None):
     """For each (b, h, i) in ``sel``: dq of query block i and dk, dv of key
     block i.  Returns (dq, dk, dv), each float64 [m, bsize, d]."""
     lib = lib or load()
+    radius = _radius(radius, window, bsize)
     q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
     batch, heads, n, d = q.shape
     s = _lens(batch, n, seqlens)
@@ -265,12 +275,13 @@ def backward_blocks(q, k, v, dout, sel, seqlens=None, bsize=32, radius=1, causal
     dq = np.empty((m, bsize, d), dtype=np.float64)
     dk = np.empty_like(dq)
     dv = np.empty_like(dq)
-    _check(lib.orc_backward_blocks_f64(batch, heads, n, d, bsize, radius, int(causal),
-                                       float(scale), _ptr(s, _i32p), _ptr(q, _f32p),
-                                       _ptr(k, _f32p), _ptr(v, _f32p), _ptr(dout, _f32p), m,
-                                       _ptr(sel, _i32p), _ptr(dq, _f64p), _ptr(dk, _f64p),
-                                       _ptr(dv, _f64p), nthreads or default_threads()),
-           "orc_backward_blocks_f64")
+    _check(lib.orc_backward_blocks_w_f64(batch, heads, n, d, bsize, radius, int(causal),
+                                         -1 if window is None else int(window), float(scale),
+                                         _ptr(s, _i32p), _ptr(q, _f32p), _ptr(k, _f32p),
+                                         _ptr(v, _f32p), _ptr(dout, _f32p), m, _ptr(sel, _i32p),
+                                         _ptr(dq, _f64p), _ptr(dk, _f64p), _ptr(dv, _f64p),
+                                         nthreads or default_threads()),
+           "orc_backward_blocks_w_f64")
     return dq, dk, dv
 
 

@@ -746,16 +746,20 @@ static int run_bpool(bjob *jb, int nthreads)
 }
 
 /* Full backward: dq, dk, dv [batch][heads][n][d] (overwritten), from the
- * forward's inputs and the output gradient dout [batch][heads][n][d]. */
-int orc_backward_f64(int batch, int heads, int n, int d, int bsize, int radius, int causal,
-                     double scale, const int32_t *seqlens, const float *q, const float *k,
-                     const float *v, const float *dout, double *dq, double *dk, double *dv,
-                     int nthreads)
+ * forward's inputs and the output gradient dout [batch][heads][n][d].  With
+ * window >= 0 the forward is the token-window one (radius = ceil(W / B)). */
+int orc_backward_w_f64(int batch, int heads, int n, int d, int bsize, int radius, int causal,
+                       int window, double scale, const int32_t *seqlens, const float *q,
+                       const float *k, const float *v, const float *dout, double *dq, double *dk,
+                       double *dv, int nthreads)
 {
     bproblem bp = {{batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v,
-                    -1},
+                    window},
                    dout};
     int rc = check_problem(&bp.fw);
+    if (rc)
+        return rc;
+    rc = check_window(window, radius, bsize);
     if (rc)
         return rc;
     const int64_t total = (int64_t)batch * heads * n * d;
@@ -778,15 +782,19 @@ int orc_backward_f64(int batch, int heads, int n, int d, int bsize, int radius, 
 
 /* Selected block indices sel[w] = (b, h, i): dq [nsel][bsize][d] gets the rows
  * of query block i, dk and dv [nsel][bsize][d] the rows of key block i. */
-int orc_backward_blocks_f64(int batch, int heads, int n, int d, int bsize, int radius, int causal,
-                            double scale, const int32_t *seqlens, const float *q, const float *k,
-                            const float *v, const float *dout, int64_t nsel, const int32_t *sel,
-                            double *dq, double *dk, double *dv, int nthreads)
+int orc_backward_blocks_w_f64(int batch, int heads, int n, int d, int bsize, int radius,
+                              int causal, int window, double scale, const int32_t *seqlens,
+                              const float *q, const float *k, const float *v, const float *dout,
+                              int64_t nsel, const int32_t *sel, double *dq, double *dk, double *dv,
+                              int nthreads)
 {
     bproblem bp = {{batch, heads, n, d, bsize, radius, causal, pick_scale(scale, d), seqlens, q, k, v,
-                    -1},
+                    window},
                    dout};
     int rc = check_problem(&bp.fw);
+    if (rc)
+        return rc;
+    rc = check_window(window, radius, bsize);
     if (rc)
         return rc;
     if (nsel < 0)
@@ -814,6 +822,25 @@ int orc_backward_blocks_f64(int batch, int heads, int n, int d, int bsize, int r
     jb.dk = dk;
     jb.dv = dv;
     return run_bpool(&jb, nthreads);
+}
+
+/* The backward entry points without a token window: the block band alone. */
+int orc_backward_f64(int batch, int heads, int n, int d, int bsize, int radius, int causal,
+                     double scale, const int32_t *seqlens, const float *q, const float *k,
+                     const float *v, const float *dout, double *dq, double *dk, double *dv,
+                     int nthreads)
+{
+    return orc_backward_w_f64(batch, heads, n, d, bsize, radius, causal, -1, scale, seqlens, q, k,
+                              v, dout, dq, dk, dv, nthreads);
+}
+
+int orc_backward_blocks_f64(int batch, int heads, int n, int d, int bsize, int radius, int causal,
+                            double scale, const int32_t *seqlens, const float *q, const float *k,
+                            const float *v, const float *dout, int64_t nsel, const int32_t *sel,
+                            double *dq, double *dk, double *dv, int nthreads)
+{
+    return orc_backward_blocks_w_f64(batch, heads, n, d, bsize, radius, causal, -1, scale, seqlens,
+                                     q, k, v, dout, nsel, sel, dq, dk, dv, nthreads);
 }
 
 /* ------------------------------------------------------------------ k-mers */

@@ -124,3 +124,90 @@ def test_window_rejects_a_band_too_narrow():
                                k.ctypes.data_as(f32p), v.ctypes.data_as(f32p),
                                out.ctypes.data_as(f64p), None, None, 1)
     assert rc == -1
+
+
+# ------------------------------------------------------------ backward pins
+
+DYADIC = 2.0 ** -7  # inputs are multiples of this; the perturbations stay exact
+
+
+def _dyadic(rng, shape, lim=1.0):
+    return (np.round(rng.uniform(-lim, lim, shape) / DYADIC) * DYADIC).astype(np.float32)
+
+
+def _fd_window(q, k, v, g, lens, bsize, window, causal, which, idx):
+    """Richardson-extrapolated central difference of sum(O * g) in one input
+    element, through the window forward."""
+    args = [q, k, v]
+
+    def at(delta):
+        a = [x.copy() for x in args]
+        a[which][idx] = np.float32(float(args[which][idx]) + delta)
+        assert float(a[which][idx]) == float(args[which][idx]) + delta
+        o, _, _ = oracle.forward(*a, lens, bsize, 0, causal, window=window, nthreads=1)
+        return float(np.sum(o * g.astype(np.float64)))
+
+    def central(h):
+        return (at(h) - at(-h)) / (2 * h)
+
+    h = 2.0 ** -10
+    return (4 * central(h / 2) - central(h)) / 3
+
+
+@pytest.mark.parametrize("bsize,nblk,window,causal,lens,d", [
+    (8, 5, 3, False, [40, 29], 8),
+    (8, 5, 9, True, [40, 19], 8),
+    (4, 8, 6, False, [32, 13], 4),
+    (16, 3, 20, True, [48, 48], 8),
+])
+def test_window_backward_matches_finite_differences(bsize, nblk, window, causal, lens, d):
+    rng = np.random.default_rng(window * 7 + nblk)
+    n = nblk * bsize
+    lens = np.array(lens, np.int32)
+    q, k, v, g = (_dyadic(rng, (len(lens), 2, n, d)) for _ in range(4))
+    dq, dk, dv = oracle.backward(q, k, v, g, lens, bsize, 0, causal, window=window, nthreads=1)
+    grads = (dq, dk, dv)
+    for which in range(3):
+        for _ in range(6):
+            b = int(rng.integers(len(lens)))
+            t = int(rng.integers(max(1, int(lens[b]))))
+            idx = (b, int(rng.integers(2)), t, int(rng.integers(d)))
+            fd = _fd_window(q, k, v, g, lens, bsize, window, causal, which, idx)
+            assert abs(grads[which][idx] - fd) <= 1e-6 * max(1.0, abs(fd)), (which, idx)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_zero_backward_closed_form(causal):
+    """W = 0: every row attends to itself alone, so O = V, dV = dO and the
+    query and key gradients vanish, exactly."""
+    rng = np.random.default_rng(11)
+    lens = np.array([64, 37], np.int32)
+    q, k, v, g = _draw(rng, 2, 3, 64, 8) + _draw(rng, 2, 3, 64, 8)[:1]
+    dq, dk, dv = oracle.backward(q, k, v, g, lens, 32, 0, causal, window=0)
+    for b, L in enumerate(lens):
+        assert np.array_equal(dv[b, :, :L], g[b, :, :L].astype(np.float64))
+        assert np.all(dq[b] == 0.0) and np.all(dk[b] == 0.0)
+        assert np.all(dv[b, :, L:] == 0.0)
+
+
+def test_window_covering_everything_backward_is_the_covering_band():
+    rng = np.random.default_rng(12)
+    lens = np.array([96, 50], np.int32)
+    q, k, v, g = _draw(rng, 2, 2, 96, 8) + _draw(rng, 2, 2, 96, 8)[:1]
+    a = oracle.backward(q, k, v, g, lens, 32, 0, False, window=96)
+    b = oracle.backward(q, k, v, g, lens, 32, 3, False)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_window_backward_blocks_match_full():
+    rng = np.random.default_rng(13)
+    lens = np.array([160, 75], np.int32)
+    q, k, v, g = _draw(rng, 2, 2, 160, 8) + _draw(rng, 2, 2, 160, 8)[:1]
+    for causal in (False, True):
+        full = oracle.backward(q, k, v, g, lens, 32, 0, causal, window=40)
+        sel = np.array([(b, h, i) for b in range(2) for h in range(2) for i in range(5)], np.int32)
+        blk = oracle.backward_blocks(q, k, v, g, sel, lens, 32, 0, causal, window=40)
+        for x, y in zip(full, blk):
+            got = np.stack([x[b, h, i * 32:(i + 1) * 32] for b, h, i in sel])
+            assert np.allclose(got, y, rtol=0, atol=1e-12)
