@@ -87,8 +87,8 @@ def code_text(src):
 
 
 BWD_SOURCES = ["block_sparse_local_amd/csrc/bwd_bf16.hip", "block_sparse_local_amd/csrc/cdna4.h",
-               "block_sparse_local_amd/csrc/launch.h"]
-KMER_SOURCES = ["block_sparse_local_amd/csrc/kmer.hip", "block_sparse_local_amd/csrc/launch.h"]
+               "block_sparse_local_amd/csrc/bwd_launch.h"]
+KMER_SOURCES = ["block_sparse_local_amd/csrc/kmer.hip", "block_sparse_local_amd/csrc/kmer_launch.h"]
 
 
 def kernel_sha():

@@ -3,7 +3,9 @@
 // synchronisation, nothing thrown across the interface.
 #include "bsl.h"
 
+#include "bwd_launch.h"
 #include "check.h"
+#include "kmer_launch.h"
 #include "launch.h"
 
 #include <hip/hip_runtime.h>
@@ -193,8 +195,6 @@ bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
     const bsl_desc &d = plan->desc;
     if (d.dtype != BSL_BF16)
         return fail(BSL_E_UNSUPPORTED, "the backward pass is built for bf16 plans only");
-    if (d.window != 0)
-        return fail(BSL_E_UNSUPPORTED, "the backward pass supports the block band only (window 0)");
     if (d.head_dim != 64 && d.head_dim != 128)
         return fail(BSL_E_UNSUPPORTED, "the backward pass supports head_dim 64 and 128 (got %d)",
                     d.head_dim);
@@ -262,7 +262,8 @@ bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
     a.heads = d.heads;
     a.n = n;
     a.head_dim = d.head_dim;
-    a.radius = d.radius;
+    a.radius = band_radius(d);
+    a.window = d.window;
     a.causal = d.causal != 0;
     a.scale = plan->scale;
     a.stream = (hipStream_t)stream;

@@ -31,7 +31,7 @@
 // zeroed in LDS before any transposing read, so NaN padding cannot leak through
 // a zero probability.
 #include "cdna4.h"
-#include "launch.h"
+#include "bwd_launch.h"
 
 #include <math.h>
 
@@ -68,6 +68,7 @@ struct BParams {
     uint16_t *dq, *dk, *dv;
     float *delta;
     int32_t heads, n, nblk, ngroups, radius, total;
+    int32_t window; // 0: the block band; >= 1: keys within this many tokens
     float c;     // scale * log2(e)
     float scale; // scale
 };
@@ -351,7 +352,10 @@ __global__ void __launch_bounds__(256) dq_kernel(BParams p)
             const bf16x8 va = row_frag<D>(vl, col, 2 * ks + half);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], dp, 0, 0, 0);
         }
-        const bool need_mask = !qvalid || pad_block || (CAUSAL && j == i);
+        // a token window also cuts blocks whose farthest pair lies beyond it
+        const int dj = j > i ? j - i : i - j;
+        const bool need_mask = !qvalid || pad_block || (CAUSAL && j == i) ||
+                               (p.window > 0 && dj * BLK + BLK - 1 > p.window);
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -362,7 +366,9 @@ __global__ void __launch_bounds__(256) dq_kernel(BParams p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = j * BLK + acc_row(r, half);
-                const bool keep = qvalid && key < len && (!CAUSAL || key <= qrow);
+                const int dist = qrow > key ? qrow - key : key - qrow;
+                const bool keep = qvalid && key < len && (!CAUSAL || key <= qrow) &&
+                                  (p.window <= 0 || dist <= p.window);
                 ds[r] = keep ? ds[r] : 0.0f;
             }
         }
@@ -530,7 +536,9 @@ __global__ void __launch_bounds__(256) dkv_kernel(BParams p)
             l4[a] = *(const f32x4 *)(lsel + 8 * a + 4 * half);
             d4[a] = *(const f32x4 *)(dl + 8 * a + 4 * half);
         }
-        const bool need_mask = !kvalid || pad_block || (CAUSAL && i == j);
+        const int di = i > j ? i - j : j - i;
+        const bool need_mask = !kvalid || pad_block || (CAUSAL && i == j) ||
+                               (p.window > 0 && di * BLK + BLK - 1 > p.window);
         float pv[16], ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -543,7 +551,9 @@ __global__ void __launch_bounds__(256) dkv_kernel(BParams p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int qr = i * BLK + acc_row(r, half);
-                const bool keep = kvalid && qr < len && (!CAUSAL || krow <= qr);
+                const int dist = qr > krow ? qr - krow : krow - qr;
+                const bool keep = kvalid && qr < len && (!CAUSAL || krow <= qr) &&
+                                  (p.window <= 0 || dist <= p.window);
                 pv[r] = keep ? pv[r] : 0.0f;
                 ds[r] = keep ? ds[r] : 0.0f;
             }
@@ -606,6 +616,7 @@ hipError_t launch_bwd_bf16(const BwdLaunch &a)
     p.nblk = a.n / BLK;
     p.ngroups = (p.nblk + 3) / 4;
     p.radius = a.radius;
+    p.window = a.window;
     p.total = a.batch * a.heads * p.ngroups;
     p.c = a.scale * LOG2E;
     p.scale = a.scale;

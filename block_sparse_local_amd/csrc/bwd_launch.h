@@ -1,0 +1,25 @@
+// bwd_launch.h -- what the C-ABI layer hands to the backward launcher (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsl {
+
+// One backward call, after argument validation.
+struct BwdLaunch {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    const int32_t *seqlens;
+    void *dq, *dk, *dv;
+    float *delta; // caller's workspace, [batch][heads][n]
+    int32_t batch, heads, n, head_dim, radius;
+    int32_t window; // 0: block band; >= 1: token window (radius = ceil(window / 32))
+    bool causal;
+    float scale;
+    hipStream_t stream;
+};
+
+hipError_t launch_bwd_bf16(const BwdLaunch &a);
+
+} // namespace bsl

@@ -21,7 +21,7 @@
 //    letters, case included -- and its validity, rolls the window ID along the
 //    8 windows and writes them as two 16-byte stores -- streaming (non-
 //    temporal) stores when the output is larger than half the Infinity Cache.
-#include "launch.h"
+#include "kmer_launch.h"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>

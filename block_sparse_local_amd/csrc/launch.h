@@ -30,40 +30,3 @@ hipError_t launch_fwd_bf16(const Launch &a);
 hipError_t launch_fwd_f32(const Launch &a);
 
 } // namespace bsl
-
-namespace bsl {
-
-// One backward call, after argument validation.
-struct BwdLaunch {
-    const void *q, *k, *v, *o, *dout;
-    const float *lse;
-    const int32_t *seqlens;
-    void *dq, *dk, *dv;
-    float *delta; // caller's workspace, [batch][heads][n]
-    int32_t batch, heads, n, head_dim, radius;
-    bool causal;
-    float scale;
-    hipStream_t stream;
-};
-
-hipError_t launch_bwd_bf16(const BwdLaunch &a);
-
-} // namespace bsl
-
-namespace bsl {
-
-// One k-mer tokenization call, after argument validation.
-struct KmerLaunch {
-    const uint8_t *bases;
-    int64_t nbytes;
-    const int64_t *starts; // device, batch + 1
-    int32_t *ids;          // device, [batch][n_out]
-    int32_t *ntok;         // device, [batch], or nullptr
-    int32_t batch, k, n_out;
-    hipStream_t stream;
-};
-
-int kmer_tiles(int32_t n_out);
-hipError_t launch_kmer(const KmerLaunch &a);
-
-} // namespace bsl

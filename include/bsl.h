@@ -74,9 +74,8 @@ typedef struct bsl_desc {
                            key s is scored for query t when |t - s| <= W,
                            over the blocks within ceil(W/32) of the query
                            block.  radius is then not used (it must still be
-                           >= 0).  Forward and packed forward only: a plan
-                           with a window gets BSL_E_UNSUPPORTED from
-                           bsl_backward. */
+                           >= 0).  Every call of the plan (forward, packed
+                           forward, backward) uses the window. */
 } bsl_desc;
 
 typedef struct bsl_plan bsl_plan;
@@ -189,10 +188,10 @@ bsl_status bsl_varlen_offsets(int32_t batch, const int32_t *lengths, int32_t *cu
  *            call overwrites it with D (0 on padded rows).  The library
  *            allocates nothing.
  * All tensors 16-byte aligned.  dq, dk, dv and delta must not overlap each
- * other or any input.  Returns BSL_E_UNSUPPORTED for an fp32 plan, a plan with
- * a token window, or head_dim 32, BSL_E_INVALID for the argument errors
- * bsl_forward rejects, a NULL pointer, misalignment or overlap, and
- * BSL_E_DEVICE if a launch fails.
+ * other or any input.  A plan with a token window differentiates the window
+ * forward.  Returns BSL_E_UNSUPPORTED for an fp32 plan or head_dim 32,
+ * BSL_E_INVALID for the argument errors bsl_forward rejects, a NULL pointer,
+ * misalignment or overlap, and BSL_E_DEVICE if a launch fails.
  * Nothing is written when an argument error is returned. */
 bsl_status bsl_backward(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
                         const void *k, const void *v, const void *o, const void *dout,

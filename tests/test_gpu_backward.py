@@ -26,10 +26,10 @@ pytestmark = pytest.mark.gpu
 MAX_TOL, MEAN_TOL = 2e-2, 2e-3
 
 
-def _gpu_backward(d, heads, dd, radius, causal):
+def _gpu_backward(d, heads, dd, radius, causal, window=0):
     q, k, v, g = (dev(d[x], "bf16") for x in ("q", "k", "v", "dout"))
     sl = lens_dev(d["seqlens"])
-    plan = bsl.Plan(head_dim=dd, heads=heads, radius=radius, causal=causal)
+    plan = bsl.Plan(head_dim=dd, heads=heads, radius=radius, causal=causal, window=window)
     o = torch.full_like(q, float("nan"))
     lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
     plan.forward(q, k, v, sl, o=o, lse=lse)
@@ -99,6 +99,57 @@ def test_backward_small(case):
                         res["o"][b, :, :L].astype(np.float64))
         assert np.max(np.abs(res["delta"][b, :, :L] - ref), initial=0.0) <= 1e-3 * max(
             1.0, np.abs(ref).max(initial=0.0))
+
+
+WINDOW_CASES = [
+    # batch, heads, n, d, window, causal, lens
+    (2, 2, 256, 64, 1, False, [256, 150]),
+    (2, 2, 256, 128, 20, True, [256, 61]),
+    (2, 2, 256, 64, 33, False, [256, 33]),
+    (3, 1, 224, 64, 64, True, [0, 1, 200]),
+    (2, 2, 320, 128, 100, False, [320, 289]),
+    (1, 2, 96, 128, 96, False, [96]),          # the window covers the sequence: dense
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES)
+def test_backward_token_window(case):
+    """The backward of a token-window plan against the oracle's window
+    backward (pinned by finite differences of the window forward)."""
+    batch, heads, n, dd, window, causal, lens = case
+    say(f"[backward] window {window} b{batch} h{heads} n{n} d{dd} causal{int(causal)} lens {lens}")
+    d = _case(batch, heads, n, dd, 0, causal, lens, seed=window * 3 + dd)
+    res = _gpu_backward(d, heads, dd, 5, causal, window=window)
+    dq, dk, dv = oracle.backward(d["q"], d["k"], d["v"], d["dout"], d["seqlens"], 32, 0, causal,
+                                 window=window)
+    _compare("dq", res["dq"], dq, d["seqlens"])
+    _compare("dk", res["dk"], dk, d["seqlens"])
+    _compare("dv", res["dv"], dv, d["seqlens"])
+
+
+def test_backward_token_window_full_size_sampled():
+    """The long-context shape (16 heads, d 128, 131072 rows, a 120000-token
+    sequence) with W = 256: sampled blocks of dQ, dK, dV against the oracle."""
+    heads, n, dd, window, L = 16, 131072, 128, 256, 120000
+    say(f"[backward] window {window} full size 1 x {heads} x {n} x {dd}, length {L}")
+    lens = np.array([L], np.int32)
+    q, k, v, g = inputs.draw(2025, 93, 1, heads, n, dd, 1.0, True, lens, poison=True, tensors=4)
+    d = dict(q=q, k=k, v=v, dout=g, seqlens=lens, n=n)
+    res = _gpu_backward(d, heads, dd, 0, False, window=window)
+    nb = (L + 31) // 32
+    rng = np.random.default_rng([2025, 93])
+    blocks = sorted({0, 1, nb - 2, nb - 1} | set(int(x) for x in rng.choice(nb, 12, replace=False)))
+    sel = np.array([(0, h, i) for h in range(heads) for i in blocks], np.int32)
+    rq, rk, rv = oracle.backward_blocks(q, k, v, g, sel, lens, 32, 0, False, window=window)
+    for name, ref in (("dq", rq), ("dk", rk), ("dv", rv)):
+        got = np.stack([res[name][b, h, i * 32:(i + 1) * 32] for b, h, i in sel])
+        rows = np.array([[i * 32 + r for r in range(32)] for _, _, i in sel])
+        valid = rows < L
+        assert np.all(got[~valid] == 0.0)
+        e = np.abs(got[valid].astype(np.float64) - ref[valid])
+        s = max(1.0, float(np.sqrt(np.mean(ref[valid] ** 2))))
+        say(f"  {name}: max-abs {e.max():.3e} mean-abs {e.mean():.3e} (ref rms {s:.3g})")
+        assert e.max() <= MAX_TOL * s and e.mean() <= MEAN_TOL * s
 
 
 def test_backward_c3_reduced():

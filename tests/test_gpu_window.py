@@ -15,7 +15,7 @@ Checked here, through the C ABI:
     covers the buffer (no token mask is then needed anywhere);
   * the 131072-token, 16-head, d 128 shape with W = 256 (the same eight-block
     band), sampled query blocks on every head against the oracle;
-  * the backward pass refuses a window plan.
+  * (the backward of a window plan: test_gpu_backward.py).
 """
 import numpy as np
 import pytest
@@ -142,20 +142,6 @@ def test_window_full_size_sampled():
     assert np.all(np.isneginf(gl[~valid]))
     assert np.max(np.abs(gl[valid] - lb[valid])) <= LSE_TOL["bf16"]
     check_rows(res["o"], None, lens, "bf16", "window full size")
-
-
-def test_window_plan_backward_is_unsupported():
-    plan = bsl.Plan(head_dim=64, heads=1, radius=1, window=40)
-    x = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device="cuda")
-    lse = torch.zeros((1, 1, 64), dtype=torch.float32, device="cuda")
-    dq = torch.full_like(x, float("nan"))
-    with pytest.raises(bsl.BslError) as err:
-        plan.backward(x, x, x, x, x, lse, dq=dq)
-    assert err.value.status == bsl.BSL_E_UNSUPPORTED
-    assert "window" in str(err.value)
-    torch.cuda.synchronize()
-    assert torch.isnan(dq).all()   # nothing written
-    plan.close()
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
