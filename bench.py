@@ -216,9 +216,10 @@ def copy_bandwidth(reps=10):
             "what": "1 GiB device-to-device copy (torch), read + written bytes over time"}
 
 
-def time_backward(key, steps, warmup, log=print):
+def time_backward(key, steps, warmup, log=print, window=0):
     """The backward pass (bsl_backward) on the workload's inputs and a seeded
-    output gradient, after one forward that supplies O and lse."""
+    output gradient, after one forward that supplies O and lse; window >= 1
+    differentiates the token-window forward instead of the block band."""
     import torch
     from block_sparse_local_amd import bsl, inputs, workload
 
@@ -227,14 +228,14 @@ def time_backward(key, steps, warmup, log=print):
     lens = d["seqlens"]
     q, k, v, g = (to_device(d[x], w.dtype) for x in ("q", "k", "v", "dout"))
     sl = torch.from_numpy(lens).cuda()
-    plan = bsl.Plan(w.d, w.heads, w.radius, w.causal, w.dtype)
+    plan = bsl.Plan(w.d, w.heads, w.radius, w.causal, w.dtype, window=window)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     plan.forward(q, k, v, sl, o=o, lse=lse, stream=stream)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     delta = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
-    acc = workload.account_backward(lens, w.heads, w.d, w.radius, w.causal, w.dtype)
+    acc = workload.account_backward(lens, w.heads, w.d, w.radius, w.causal, w.dtype, window)
     for _ in range(warmup):
         plan.backward(q, k, v, o, g, lse, sl, dq=dq, dk=dk, dv=dv, delta=delta, stream=stream)
     torch.cuda.synchronize()
@@ -251,8 +252,10 @@ def time_backward(key, steps, warmup, log=print):
     plan.close()
     del q, k, v, g, o, lse, dq, dk, dv, delta
     torch.cuda.empty_cache()
-    log(f"[bench] {key} backward: {wall / steps * 1e3:.3f} ms/step")
-    return dict(key=key, w=w, d=d, acc=acc, wall=wall, per_launch=per_launch, steps=steps)
+    log(f"[bench] {key} backward{f' (token window {window})' if window else ''}: "
+        f"{wall / steps * 1e3:.3f} ms/step")
+    return dict(key=key, w=w, d=d, acc=acc, wall=wall, per_launch=per_launch, steps=steps,
+                window=window)
 
 
 def cpu_baseline_backward(r, target_flops=6.0e11, log=print):
@@ -262,7 +265,8 @@ def cpu_baseline_backward(r, target_flops=6.0e11, log=print):
     import oracle
     from block_sparse_local_amd import workload
     d, w = r["d"], r["w"]
-    per_token = 10.0 * w.d * (2 * w.radius + 1) * 32 * w.heads
+    window = r.get("window", 0)
+    per_token = 10.0 * w.d * (2 * workload.band_radius(w.radius, window) + 1) * 32 * w.heads
     rows = max(32, int(target_flops / per_token) // 32 * 32)
     L = min(rows, int(d["seqlens"][0]))
     n = -(-L // 32) * 32
@@ -271,9 +275,9 @@ def cpu_baseline_backward(r, target_flops=6.0e11, log=print):
     threads = min(16, oracle.default_threads())
     t0 = time.perf_counter()
     oracle.backward(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["dout"]), lens, 32, w.radius,
-                    w.causal, nthreads=threads)
+                    w.causal, nthreads=threads, window=window if window > 0 else None)
     dt = time.perf_counter() - t0
-    acc = workload.account_backward(lens, w.heads, w.d, w.radius, w.causal, w.dtype)
+    acc = workload.account_backward(lens, w.heads, w.d, w.radius, w.causal, w.dtype, window)
     log(f"[bench] oracle backward: {w.heads} heads x {L} tokens in {dt:.1f}s")
     return {"value": acc["useful_flops"] / dt / 1e12, "unit": "TFLOP/s",
             "cores": min(threads, w.heads), "kind": "oracle",
@@ -555,6 +559,16 @@ def main():
                           "roofline": roofw, "detail": extraw}
         if not args.no_cpu_baseline:
             line["window"]["cpu_baseline"] = cpu_baseline(rw, log=log)
+        if args.backward and r_w_dtype == "bf16":
+            rbw = time_backward(args.workload, args.steps, args.warmup, log, window=args.window)
+            tbw, roofbw, extrabw = summarize(rbw, None)
+            line["window"]["backward"] = {"ms_per_step": tbw * 1e3,
+                                          "value": extrabw["useful_tflops"], "unit": "TFLOP/s",
+                                          "tokens_per_s": extrabw["tokens_per_s"],
+                                          "roofline": roofbw, "detail": extrabw}
+            if not args.no_cpu_baseline:
+                line["window"]["backward"]["cpu_baseline"] = cpu_baseline_backward(rbw, log=log)
+            del rbw
         log(f"[bench] {args.workload} token window {args.window}: {tw * 1e3:.3f} ms/step, "
             f"{extraw['useful_tflops']:.1f} useful TFLOP/s ({roofw['frac'] * 100:.1f}% of "
             f"{roofw['bound']} peak)")

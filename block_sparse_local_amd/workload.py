@@ -89,10 +89,10 @@ def account(lens, heads, d, radius, causal, dtype="bf16", window=0):
                 bound="hbm" if t_hbm >= t_mfma else compute_unit, flops_peak=peak)
 
 
-def account_backward(lens, heads, d, radius, causal, dtype="bf16"):
+def account_backward(lens, heads, d, radius, causal, dtype="bf16", window=0):
     esz = 2 if dtype == "bf16" else 4
-    up = useful_pairs_per_head(lens, radius, causal) * heads
-    bp = block_pairs_per_head(lens, radius, causal) * heads
+    up = useful_pairs_per_head(lens, radius, causal, window) * heads
+    bp = block_pairs_per_head(lens, radius, causal, window) * heads
     tokens = int(np.sum(lens))
     flops = 10.0 * d * up
     # the kernels recompute S and dP in both the dQ and the dK/dV kernel
