@@ -216,10 +216,11 @@ def copy_bandwidth(reps=10):
             "what": "1 GiB device-to-device copy (torch), read + written bytes over time"}
 
 
-def time_backward(key, steps, warmup, log=print, window=0):
+def time_backward(key, steps, warmup, log=print, window=0, layout="padded"):
     """The backward pass (bsl_backward) on the workload's inputs and a seeded
     output gradient, after one forward that supplies O and lse; window >= 1
-    differentiates the token-window forward instead of the block band."""
+    differentiates the token-window forward instead of the block band, and
+    layout "packed" times bsl_backward_varlen on the same sequences packed."""
     import torch
     from block_sparse_local_amd import bsl, inputs, workload
 
@@ -229,22 +230,39 @@ def time_backward(key, steps, warmup, log=print, window=0):
     q, k, v, g = (to_device(d[x], w.dtype) for x in ("q", "k", "v", "dout"))
     sl = torch.from_numpy(lens).cuda()
     plan = bsl.Plan(w.d, w.heads, w.radius, w.causal, w.dtype, window=window)
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    plan.forward(q, k, v, sl, o=o, lse=lse, stream=stream)
+    if layout == "packed":
+        q, k, v, g = (pack_device(x, lens) for x in (q, k, v, g))
+        cu_host, max_len, _ = bsl.bsl_varlen_offsets(lens)
+        cu = torch.from_numpy(cu_host).cuda()
+        o = torch.empty_like(q)
+        lse = torch.empty((w.heads, q.shape[0]), dtype=torch.float32, device="cuda")
+        plan.forward_varlen(q, k, v, cu, max_len, o=o, lse=lse, stream=stream)
+        delta = torch.empty((w.heads, q.shape[0]), dtype=torch.float32, device="cuda")
+    else:
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+        plan.forward(q, k, v, sl, o=o, lse=lse, stream=stream)
+        delta = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    delta = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+
+    def call():
+        if layout == "packed":
+            plan.backward_varlen(q, k, v, o, g, lse, cu, max_len, dq=dq, dk=dk, dv=dv,
+                                 delta=delta, stream=stream)
+        else:
+            plan.backward(q, k, v, o, g, lse, sl, dq=dq, dk=dk, dv=dv, delta=delta,
+                          stream=stream)
     acc = workload.account_backward(lens, w.heads, w.d, w.radius, w.causal, w.dtype, window)
     for _ in range(warmup):
-        plan.backward(q, k, v, o, g, lse, sl, dq=dq, dk=dk, dv=dv, delta=delta, stream=stream)
+        call()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t_begin = time.perf_counter()
     for s in range(steps):
         starts[s].record(stream)
-        plan.backward(q, k, v, o, g, lse, sl, dq=dq, dk=dk, dv=dv, delta=delta, stream=stream)
+        call()
         ends[s].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_begin
@@ -252,10 +270,10 @@ def time_backward(key, steps, warmup, log=print, window=0):
     plan.close()
     del q, k, v, g, o, lse, dq, dk, dv, delta
     torch.cuda.empty_cache()
-    log(f"[bench] {key} backward{f' (token window {window})' if window else ''}: "
-        f"{wall / steps * 1e3:.3f} ms/step")
+    log(f"[bench] {key} backward{f' (token window {window})' if window else ''}"
+        f"{' (packed)' if layout == 'packed' else ''}: {wall / steps * 1e3:.3f} ms/step")
     return dict(key=key, w=w, d=d, acc=acc, wall=wall, per_launch=per_launch, steps=steps,
-                window=window)
+                window=window, layout=layout)
 
 
 def cpu_baseline_backward(r, target_flops=6.0e11, log=print):
@@ -545,6 +563,14 @@ def main():
         if not args.no_cpu_baseline:
             # the oracle has one layout: the same sequences, the same operation
             line["varlen"]["cpu_baseline"] = cpu_baseline(rv, log=log)
+        if args.backward and r_w_dtype == "bf16":
+            rbv = time_backward(args.workload, args.steps, args.warmup, log, layout="packed")
+            tbv, roofbv, extrabv = summarize(rbv, None)
+            line["varlen"]["backward"] = {"ms_per_step": tbv * 1e3,
+                                          "value": extrabv["useful_tflops"], "unit": "TFLOP/s",
+                                          "tokens_per_s": extrabv["tokens_per_s"],
+                                          "roofline": roofbv, "detail": extrabv}
+            del rbv
         log(f"[bench] {args.workload} packed: {tv * 1e3:.3f} ms/step "
             f"({roofv['frac'] * 100:.1f}% of {roofv['bound']} peak); buffers "
             f"{rv['buffer_bytes'] / 2**20:.1f} MiB vs {padded_bytes / 2**20:.1f} MiB padded")

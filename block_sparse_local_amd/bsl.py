@@ -24,8 +24,8 @@ BSL_BF16, BSL_F32 = 0, 1
 
 # every function include/bsl.h declares
 EXPORTS = ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_forward_varlen",
-           "bsl_varlen_offsets", "bsl_backward", "bsl_kmer_tokenize", "bsl_kmer_ceiling",
-           "bsl_check_seqlens", "bsl_check_cu_seqlens", "bsl_destroy", "bsl_status_string",
+           "bsl_varlen_offsets", "bsl_backward", "bsl_backward_varlen", "bsl_kmer_tokenize",
+           "bsl_kmer_ceiling", "bsl_check_seqlens", "bsl_check_cu_seqlens", "bsl_destroy", "bsl_status_string",
            "bsl_last_error", "bsl_version")
 
 
@@ -73,6 +73,8 @@ def load(path=LIB_PATH):
     i32p = ctypes.POINTER(i32)
     lib.bsl_varlen_offsets.argtypes = [i32, i32p, i32p, i32p, i32p]
     lib.bsl_backward.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.bsl_backward_varlen.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        vp, vp]
     lib.bsl_kmer_tokenize.argtypes = [i32, vp, ctypes.c_int64, vp, i32, i32, vp, vp, vp]
     lib.bsl_kmer_ceiling.argtypes = [i32, ctypes.POINTER(ctypes.c_int64), i32, ctypes.POINTER(i32)]
     lib.bsl_check_seqlens.argtypes = [i32, i32, vp, vp, vp]
@@ -85,8 +87,8 @@ def load(path=LIB_PATH):
     lib.bsl_version.argtypes = []
     lib.bsl_version.restype = i32
     for name in ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_forward_varlen",
-                 "bsl_varlen_offsets", "bsl_backward", "bsl_kmer_tokenize", "bsl_kmer_ceiling",
-                 "bsl_check_seqlens", "bsl_check_cu_seqlens", "bsl_destroy"):
+                 "bsl_varlen_offsets", "bsl_backward", "bsl_backward_varlen", "bsl_kmer_tokenize",
+                 "bsl_kmer_ceiling", "bsl_check_seqlens", "bsl_check_cu_seqlens", "bsl_destroy"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -160,6 +162,13 @@ def bsl_backward(plan, batch, n, q, k, v, o, dout, lse, seqlens, dq, dk, dv, del
     _check(load().bsl_backward(plan, batch, n, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
                                _ptr(lse), _ptr(seqlens), _ptr(dq), _ptr(dk), _ptr(dv),
                                _ptr(delta), _stream(stream)))
+
+
+def bsl_backward_varlen(plan, batch, tokens, max_seqlen, q, k, v, o, dout, lse, cu_seqlens, dq,
+                        dk, dv, delta, stream=None):
+    _check(load().bsl_backward_varlen(plan, batch, tokens, max_seqlen, _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(o), _ptr(dout), _ptr(lse), _ptr(cu_seqlens), _ptr(dq),
+                                      _ptr(dk), _ptr(dv), _ptr(delta), _stream(stream)))
 
 
 def bsl_kmer_tokenize(batch, bases, nbytes, starts, k, n_out, ids, ntok=None, stream=None):
@@ -342,6 +351,35 @@ class Plan:
         bsl_forward_varlen(self.handle, cu_seqlens.shape[0] - 1, q.shape[0], max_seqlen, q, k, v,
                            o, cu_seqlens, lse, stream)
         return o
+
+    def backward_varlen(self, q, k, v, o, dout, lse, cu_seqlens, max_seqlen, dq=None, dk=None,
+                        dv=None, delta=None, stream=None):
+        """Packed layout: q, k, v, o, dout, dq, dk, dv [tokens, heads, head_dim];
+        lse and delta float32 [heads, tokens].  Returns (dq, dk, dv); rows outside
+        every sequence keep what dq, dk, dv held.  See bsl_backward_varlen in
+        include/bsl.h."""
+        import torch
+        dq = torch.zeros_like(q) if dq is None else dq
+        dk = torch.zeros_like(q) if dk is None else dk
+        dv = torch.zeros_like(q) if dv is None else dv
+        if delta is None:
+            delta = torch.empty((self.heads, q.shape[0]), dtype=torch.float32, device=q.device)
+        if q.dim() != 3 or q.shape[1] != self.heads or q.shape[2] != self.head_dim:
+            raise ValueError(f"q must be [tokens, {self.heads}, {self.head_dim}]")
+        for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk),
+                        ("dv", dv)):
+            if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous tensor like q")
+        for name, t in (("lse", lse), ("delta", delta)):
+            if (t.dtype != torch.float32 or t.shape != (self.heads, q.shape[0])
+                    or not t.is_contiguous()):
+                raise ValueError(f"{name} must be a contiguous float32 tensor of shape "
+                                 "[heads, tokens]")
+        if (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1):
+            raise ValueError("cu_seqlens must be an int32 CUDA tensor of shape [batch + 1]")
+        bsl_backward_varlen(self.handle, cu_seqlens.shape[0] - 1, q.shape[0], max_seqlen, q, k, v,
+                            o, dout, lse, cu_seqlens, dq, dk, dv, delta, stream)
+        return dq, dk, dv
 
     def backward(self, q, k, v, o, dout, lse, seqlens=None, dq=None, dk=None, dv=None,
                  delta=None, stream=None):

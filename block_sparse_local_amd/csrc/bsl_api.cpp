@@ -254,6 +254,8 @@ bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
     a.dout = dout;
     a.lse = lse;
     a.seqlens = seqlens;
+    a.cu_seqlens = nullptr;
+    a.tokens = 0;
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
@@ -261,6 +263,98 @@ bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
     a.batch = batch;
     a.heads = d.heads;
     a.n = n;
+    a.head_dim = d.head_dim;
+    a.radius = band_radius(d);
+    a.window = d.window;
+    a.causal = d.causal != 0;
+    a.scale = plan->scale;
+    a.stream = (hipStream_t)stream;
+    const hipError_t e = bsl::launch_bwd_bf16(a);
+    if (e != hipSuccess)
+        return fail(BSL_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    return BSL_OK;
+}
+
+bsl_status run_backward_varlen(const bsl_plan *plan, int32_t batch, int32_t tokens,
+                               int32_t max_seqlen, const void *q, const void *k, const void *v,
+                               const void *o, const void *dout, const float *lse,
+                               const int32_t *cu_seqlens, void *dq, void *dk, void *dv,
+                               float *delta, void *stream)
+{
+    if (!plan)
+        return fail(BSL_E_INVALID, "plan is NULL");
+    const bsl_desc &d = plan->desc;
+    if (d.dtype != BSL_BF16)
+        return fail(BSL_E_UNSUPPORTED, "the backward pass is built for bf16 plans only");
+    if (d.head_dim != 64 && d.head_dim != 128)
+        return fail(BSL_E_UNSUPPORTED, "the backward pass supports head_dim 64 and 128 (got %d)",
+                    d.head_dim);
+    if (batch < 0 || tokens < 0 || max_seqlen < 0)
+        return fail(BSL_E_INVALID, "batch (%d), tokens (%d) and max_seqlen (%d) must be >= 0",
+                    batch, tokens, max_seqlen);
+    if (batch == 0 || tokens == 0 || max_seqlen == 0)
+        return BSL_OK;
+    if (!cu_seqlens)
+        return fail(BSL_E_INVALID, "cu_seqlens must be a non-NULL device pointer");
+    const void *ins[] = {q, k, v, o, dout, lse};
+    void *outs[] = {dq, dk, dv, delta};
+    for (const void *x : ins)
+        if (!x)
+            return fail(BSL_E_INVALID, "q, k, v, o, dout and lse must be non-NULL device pointers");
+    for (const void *x : outs)
+        if (!x)
+            return fail(BSL_E_INVALID, "dq, dk, dv and delta must be non-NULL device pointers");
+    for (const void *x : ins)
+        if (!aligned16(x))
+            return fail(BSL_E_INVALID, "every tensor must be 16-byte aligned");
+    for (const void *x : outs)
+        if (!aligned16(x))
+            return fail(BSL_E_INVALID, "every tensor must be 16-byte aligned");
+    const long double elems = (long double)tokens * d.heads * (long double)d.head_dim;
+    if (elems > 9.0e18L)
+        return fail(BSL_E_INVALID, "tensor of %d x %d x %d elements is too large", tokens,
+                    d.heads, d.head_dim);
+    const long long nblk = ((long long)max_seqlen + d.block_size - 1) / d.block_size;
+    if ((long long)batch * d.heads * nblk > 0x7fffffffLL ||
+        (long long)d.heads * tokens > 0x7fffffffLL)
+        return fail(BSL_E_INVALID, "batch * heads * ceil(max_seqlen / 32) or heads * tokens "
+                                   "exceeds 2^31 - 1");
+    const size_t tb = (size_t)elems * 2;                          // one bf16 tensor
+    const size_t rb = (size_t)d.heads * (size_t)tokens * 4;       // one float row vector
+    const size_t in_bytes[] = {tb, tb, tb, tb, tb, rb};
+    const size_t out_bytes[] = {tb, tb, tb, rb};
+    for (int a = 0; a < 4; ++a) {
+        for (int b = 0; b < 6; ++b)
+            if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b]))
+                return fail(BSL_E_INVALID, "dq, dk, dv and delta must not overlap any input");
+        for (int b = a + 1; b < 4; ++b)
+            if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b]))
+                return fail(BSL_E_INVALID, "dq, dk, dv and delta must not overlap each other");
+    }
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return fail(BSL_E_DEVICE, "hipGetDevice failed");
+    if (dev != plan->device)
+        return fail(BSL_E_INVALID, "current device %d is not the plan's device %d", dev,
+                    plan->device);
+
+    bsl::BwdLaunch a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.seqlens = nullptr;
+    a.cu_seqlens = cu_seqlens;
+    a.tokens = tokens;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.delta = delta;
+    a.batch = batch;
+    a.heads = d.heads;
+    a.n = max_seqlen;
     a.head_dim = d.head_dim;
     a.radius = band_radius(d);
     a.window = d.window;
@@ -364,6 +458,16 @@ bsl_status bsl_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
                         float *delta, void *stream)
 {
     return run_backward(plan, batch, n, q, k, v, o, dout, lse, seqlens, dq, dk, dv, delta, stream);
+}
+
+bsl_status bsl_backward_varlen(const bsl_plan *plan, int32_t batch, int32_t tokens,
+                               int32_t max_seqlen, const void *q, const void *k, const void *v,
+                               const void *o, const void *dout, const float *lse,
+                               const int32_t *cu_seqlens, void *dq, void *dk, void *dv,
+                               float *delta, void *stream)
+{
+    return run_backward_varlen(plan, batch, tokens, max_seqlen, q, k, v, o, dout, lse, cu_seqlens,
+                               dq, dk, dv, delta, stream);
 }
 
 bsl_status bsl_forward_varlen(const bsl_plan *plan, int32_t batch, int32_t tokens,

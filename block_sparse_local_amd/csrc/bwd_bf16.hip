@@ -64,7 +64,9 @@ struct BTile {
 struct BParams {
     const uint16_t *q, *k, *v, *o, *dout;
     const float *lse;
-    const int32_t *seqlens;
+    const int32_t *seqlens; // padded layout: lengths (or nullptr)
+    const int32_t *cu;      // packed layout: sequence start offsets, batch + 1 of them
+    int32_t tokens;         // packed layout: rows in the buffers
     uint16_t *dq, *dk, *dv;
     float *delta;
     int32_t heads, n, nblk, ngroups, radius, total;
@@ -73,11 +75,38 @@ struct BParams {
     float scale; // scale
 };
 
-__device__ __forceinline__ int seq_len(const BParams &p, int b)
-{
-    int len = p.seqlens ? p.seqlens[b] : p.n;
-    return len < 0 ? 0 : (len > p.n ? p.n : len);
-}
+// Where sequence b's rows of head h live and how many are real.  Padded layout
+// [batch][heads][n][D]: rows D apart; lse and delta [batch][heads][n].  Packed
+// layout [tokens][heads][D]: rows heads D apart from (cu[b] heads + h) D; lse
+// and delta [heads][tokens].  Offsets read from the device are clamped so that
+// every row index below stays inside the buffers whatever they hold.
+template <int D, bool VARLEN>
+struct BSeq {
+    size_t base, lbase, rs;
+    int len;
+    __device__ __forceinline__ BSeq(const BParams &p, int b, int h)
+    {
+        if (VARLEN) {
+            int s0 = p.cu[b], s1 = p.cu[b + 1];
+            s0 = s0 < 0 ? 0 : (s0 > p.tokens ? p.tokens : s0);
+            s1 = s1 < s0 ? s0 : (s1 > p.tokens ? p.tokens : s1);
+            len = s1 - s0 > p.n ? p.n : s1 - s0;
+            base = ((size_t)s0 * (size_t)p.heads + (size_t)h) * D;
+            lbase = (size_t)h * (size_t)p.tokens + (size_t)s0;
+            rs = (size_t)p.heads * D;
+        } else {
+            len = p.seqlens ? p.seqlens[b] : p.n;
+            len = len < 0 ? 0 : (len > p.n ? p.n : len);
+            base = ((size_t)b * p.heads + h) * (size_t)p.n * D;
+            lbase = ((size_t)b * p.heads + h) * (size_t)p.n;
+            rs = D;
+        }
+    }
+};
+
+// Fourth word of a raw buffer resource on gfx9-family GPUs (32-bit data
+// format, no swizzle, no index stride).
+constexpr int BUFFER_WORD3 = 0x00020000;
 
 // ------------------------------------------------------------ shared parts
 // Band of block x (a query block for dq, a key block for dkv) within nb real
@@ -101,16 +130,20 @@ __device__ __forceinline__ void band_of(int x, int nb, int R, bool causal, bool 
 // Buffer loads into LDS: a scalar buffer resource based at the block's first
 // row of each tile (bounds-checked against the block) plus a per-lane offset
 // that does not depend on the block, so no vector ALU goes into addresses.
-template <int D, int NT, int LPT>
+// Rows are rs elements apart; rows past `last` (the block's last row inside the
+// sequence, packed layout) repeat it, so no load leaves the sequence; their
+// values are zeroed or masked before use.
+template <int D, int NT, int LPT, bool VARLEN>
 __device__ __forceinline__ void issue_pair(uint8_t *stage, const uint16_t *ga, const uint16_t *gb,
-                                          int row0, int tid, int wave)
+                                          int row0, size_t rs, int last, int tid, int wave)
 {
     using T = BTile<D>;
     constexpr int SLOTS = 2 * T::BYTES / 16;
+    const int bytes = (int)((size_t)(last + 1) * rs * 2);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(ga + (size_t)row0 * D), (short)0, T::BYTES, 0x00020000);
+        (void *)(ga + (size_t)row0 * rs), (short)0, bytes, BUFFER_WORD3);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(gb + (size_t)row0 * D), (short)0, T::BYTES, 0x00020000);
+        (void *)(gb + (size_t)row0 * rs), (short)0, bytes, BUFFER_WORD3);
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
         const int s = u * NT + tid;
@@ -118,7 +151,8 @@ __device__ __forceinline__ void issue_pair(uint8_t *stage, const uint16_t *ga, c
         const int t = second ? s - SLOTS / 2 : s;
         const int r = t / T::CPR, cp = t % T::CPR;
         const int c = cp ^ T::swz(r);
-        const uint32_t off = (uint32_t)(r * D + c * 8) * 2u;
+        const int rr = VARLEN && r > last ? last : r;
+        const uint32_t off = (uint32_t)((size_t)rr * rs + (size_t)c * 8) * 2u;
         uint8_t *dst = stage + (u * NT + wave * 64) * 16;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? rb : ra, (lds_void *)dst, 16, off, 0, 0, 0);
     }
@@ -177,7 +211,7 @@ __device__ __forceinline__ void pack_b(const float *x, bf16x8 &b0, bf16x8 &b1)
 // `row` of `out` (already offset to the slice), scaled; zeros when !valid.
 template <int NMT>
 __device__ __forceinline__ void store_rowT(uint16_t *out_row, const f32x16 *acc, float mul, bool valid,
-                                           int half)
+                                           int half, bool store = true)
 {
     // lanes l and l + 32 hold the two 4-element halves of each 8-element run;
     // one exchange gives each lane two whole runs, stored 16 bytes at a time
@@ -205,13 +239,14 @@ __device__ __forceinline__ void store_rowT(uint16_t *out_row, const f32x16 *acc,
             got[1] = (uint32_t)__shfl_xor((int)give[1], 32);
             const u32x4 run = half ? u32x4{got[0], got[1], mine[0], mine[1]}
                                    : u32x4{mine[0], mine[1], got[0], got[1]};
-            *(u32x4 *)(out_row + m * 32 + 8 * (2 * k + half)) = run;
+            if (store)
+                *(u32x4 *)(out_row + m * 32 + 8 * (2 * k + half)) = run;
         }
     }
 }
 
 // ------------------------------------------------------------------- dq
-template <int D, int NSTAGE, bool CAUSAL>
+template <int D, int NSTAGE, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(256) dq_kernel(BParams p)
 {
     using T = BTile<D>;
@@ -228,23 +263,26 @@ __global__ void __launch_bounds__(256) dq_kernel(BParams p)
     const int col = lane & 31, half = lane >> 5;
 
     const int g = xcd_contiguous((int)blockIdx.x, p.total);
-    const int grp = g % p.ngroups, bh = g / p.ngroups, b = bh / p.heads;
-    const int len = seq_len(p, b);
+    const int grp = g % p.ngroups, bh = g / p.ngroups, b = bh / p.heads, h = bh % p.heads;
+    const BSeq<D, VARLEN> sq(p, b, h);
+    const int len = sq.len;
     const int nb = (len + BLK - 1) / BLK;
     const int R = p.radius;
     const int i0 = grp * MQ, i = i0 + wave;
-    const bool exists = i < p.nblk;
-    const size_t base = (size_t)bh * (size_t)p.n * D;
+    // packed layout: rows past the sequence belong to the next one, so only
+    // the sequence's own blocks exist; padded layout: every block of the buffer
+    const bool exists = i < (VARLEN ? nb : p.nblk);
+    const size_t base = sq.base, RS = sq.rs;
     const int qrow = i * BLK + col;
     const bool qvalid = exists && qrow < len;
-    uint16_t *dq_row = p.dq + base + (size_t)qrow * D;
+    uint16_t *dq_row = p.dq + base + (size_t)qrow * RS;
 
     if (i0 >= nb) { // a group of padding only
-        if (exists) {
+        if (!VARLEN && exists) {
             for (int c = lane; c < BLK * D / 8; c += 64)
                 *(u32x4 *)(p.dq + base + (size_t)i * BLK * D + (size_t)c * 8) = u32x4{0, 0, 0, 0};
             if (half == 0)
-                p.delta[(size_t)bh * p.n + qrow] = 0.0f;
+                p.delta[sq.lbase + qrow] = 0.0f;
         }
         return;
     }
@@ -264,7 +302,9 @@ __global__ void __launch_bounds__(256) dq_kernel(BParams p)
     };
     const uint16_t *const kg = p.k + base, *const vg = p.v + base;
     auto issue = [&](int j, int stage) {
-        issue_pair<D, NT, LPT>(lds + stage * STAGE, kg, vg, j * BLK, tid, wave);
+        const int last = len - 1 - j * BLK < BLK - 1 ? len - 1 - j * BLK : BLK - 1;
+        issue_pair<D, NT, LPT, VARLEN>(lds + stage * STAGE, kg, vg, j * BLK, RS,
+                                       VARLEN ? last : BLK - 1, tid, wave);
     };
 
     // this wave's query fragments, lse (log2 units) and D
@@ -273,13 +313,13 @@ __global__ void __launch_bounds__(256) dq_kernel(BParams p)
     for (int s = 0; s < NKS; ++s) {
         u32x4 x = u32x4{0, 0, 0, 0}, y = u32x4{0, 0, 0, 0};
         if (qvalid) {
-            x = *(const u32x4 *)(p.q + base + (size_t)qrow * D + s * 16 + half * 8);
-            y = *(const u32x4 *)(p.dout + base + (size_t)qrow * D + s * 16 + half * 8);
+            x = *(const u32x4 *)(p.q + base + (size_t)qrow * RS + s * 16 + half * 8);
+            y = *(const u32x4 *)(p.dout + base + (size_t)qrow * RS + s * 16 + half * 8);
         }
         qf[s] = as_bf16x8(x);
         gf[s] = as_bf16x8(y);
     }
-    const float lse2 = qvalid ? p.lse[(size_t)bh * p.n + qrow] * LOG2E : 0.0f;
+    const float lse2 = qvalid ? p.lse[sq.lbase + qrow] * LOG2E : 0.0f;
     // D_t = sum_c dO_tc O_tc: this lane's half of the row (the dO fragments it
     // holds) against the same elements of O, then the other half from lane +- 32;
     // written for the key-stationary kernel, 0 on rows past the length
@@ -288,15 +328,15 @@ __global__ void __launch_bounds__(256) dq_kernel(BParams p)
     for (int s = 0; s < NKS; ++s) {
         u32x4 z = u32x4{0, 0, 0, 0};
         if (qvalid)
-            z = *(const u32x4 *)(p.o + base + (size_t)qrow * D + s * 16 + half * 8);
+            z = *(const u32x4 *)(p.o + base + (size_t)qrow * RS + s * 16 + half * 8);
         const bf16x8 ov = as_bf16x8(z);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             Dt = fmaf((float)gf[s][e], (float)ov[e], Dt);
     }
     Dt += __shfl_xor(Dt, 32);
-    if (exists && half == 0)
-        p.delta[(size_t)bh * p.n + qrow] = Dt;
+    if ((VARLEN ? qvalid : exists) && half == 0)
+        p.delta[sq.lbase + qrow] = Dt;
 
 #pragma unroll
     for (int a = 0; a < NSTAGE - 1; ++a)
@@ -383,11 +423,11 @@ __global__ void __launch_bounds__(256) dq_kernel(BParams p)
         }
     }
     if (exists)
-        store_rowT<NMT>(dq_row, acc, p.scale, qvalid, half);
+        store_rowT<NMT>(dq_row, acc, p.scale, qvalid, half, !VARLEN || qvalid);
 }
 
 // ------------------------------------------------------------------ dkv
-template <int D, int NSTAGE, bool CAUSAL>
+template <int D, int NSTAGE, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(256) dkv_kernel(BParams p)
 {
     using T = BTile<D>;
@@ -405,21 +445,22 @@ __global__ void __launch_bounds__(256) dkv_kernel(BParams p)
     const int col = lane & 31, half = lane >> 5;
 
     const int g = xcd_contiguous((int)blockIdx.x, p.total);
-    const int grp = g % p.ngroups, bh = g / p.ngroups, b = bh / p.heads;
-    const int len = seq_len(p, b);
+    const int grp = g % p.ngroups, bh = g / p.ngroups, b = bh / p.heads, h = bh % p.heads;
+    const BSeq<D, VARLEN> sq(p, b, h);
+    const int len = sq.len;
     const int nb = (len + BLK - 1) / BLK;
     const int R = p.radius;
     const int j0 = grp * MK, j = j0 + wave;
-    const bool exists = j < p.nblk;
-    const size_t base = (size_t)bh * (size_t)p.n * D;
-    const size_t rbase = (size_t)bh * (size_t)p.n; // lse, delta
+    const bool exists = j < (VARLEN ? nb : p.nblk);
+    const size_t base = sq.base, RS = sq.rs;
+    const size_t rbase = sq.lbase; // lse, delta
     const int krow = j * BLK + col;
     const bool kvalid = exists && krow < len;
-    uint16_t *dk_row = p.dk + base + (size_t)krow * D;
-    uint16_t *dv_row = p.dv + base + (size_t)krow * D;
+    uint16_t *dk_row = p.dk + base + (size_t)krow * RS;
+    uint16_t *dv_row = p.dv + base + (size_t)krow * RS;
 
     if (j0 >= nb) {
-        if (exists)
+        if (!VARLEN && exists)
             for (int c = lane; c < BLK * D / 8; c += 64) {
                 const size_t off = base + (size_t)j * BLK * D + (size_t)c * 8;
                 *(u32x4 *)(p.dk + off) = u32x4{0, 0, 0, 0};
@@ -439,16 +480,22 @@ __global__ void __launch_bounds__(256) dkv_kernel(BParams p)
         const int x = t + rot;
         return ilo + (x >= L ? x - L : x);
     };
-    // Q and dO tiles by every thread; lse and D (32 floats each) by lanes 0-15
-    // of wave 0, which therefore has one more load in flight per stage
+    // Q and dO tiles by every thread; lse (wave 0) and D (wave 1), 32 floats
+    // each, by lanes 0-7, so waves 0 and 1 have one more load in flight per
+    // stage.  All are buffer loads bounded by the block's rows inside the
+    // sequence.
     const uint16_t *const qg = p.q + base, *const gg = p.dout + base;
     const float *const lg = p.lse + rbase, *const dg = p.delta + rbase;
     auto issue = [&](int i, int stage) {
         uint8_t *st = lds + stage * STAGE;
-        issue_pair<D, NT, LPT>(st, qg, gg, i * BLK, tid, wave);
-        if (wave == 0 && lane < 16) {
-            const float *src = (lane < 8 ? lg : dg) + i * BLK + (lane & 7) * 4;
-            __builtin_amdgcn_global_load_lds(src, (lds_void *)(st + TILES), 16, 0, 0);
+        const int last_in = len - 1 - i * BLK < BLK - 1 ? len - 1 - i * BLK : BLK - 1;
+        const int last = VARLEN ? last_in : BLK - 1;
+        issue_pair<D, NT, LPT, VARLEN>(st, qg, gg, i * BLK, RS, last, tid, wave);
+        if (wave < 2 && lane < 8) {
+            const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)((wave == 0 ? lg : dg) + i * BLK), (short)0, (last + 1) * 4, BUFFER_WORD3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void *)(st + TILES + wave * BLK * 4), 16,
+                                                     (uint32_t)lane * 16u, 0, 0, 0);
         }
     };
 
@@ -458,8 +505,8 @@ __global__ void __launch_bounds__(256) dkv_kernel(BParams p)
     for (int s = 0; s < NKS; ++s) {
         u32x4 x = u32x4{0, 0, 0, 0}, y = u32x4{0, 0, 0, 0};
         if (kvalid) {
-            x = *(const u32x4 *)(p.k + base + (size_t)krow * D + s * 16 + half * 8);
-            y = *(const u32x4 *)(p.v + base + (size_t)krow * D + s * 16 + half * 8);
+            x = *(const u32x4 *)(p.k + base + (size_t)krow * RS + s * 16 + half * 8);
+            y = *(const u32x4 *)(p.v + base + (size_t)krow * RS + s * 16 + half * 8);
         }
         kf[s] = as_bf16x8(x);
         vf[s] = as_bf16x8(y);
@@ -488,7 +535,7 @@ __global__ void __launch_bounds__(256) dkv_kernel(BParams p)
         const int i = block_at(t);
         const int stage = t % NSTAGE;
         if (t + NSTAGE - 2 < L) {
-            if (wave == 0)
+            if (wave < 2)
                 wait_vm_lgkm0<(NSTAGE - 2) * (LPT + 1)>();
             else
                 wait_vm_lgkm0<(NSTAGE - 2) * LPT>();
@@ -577,22 +624,28 @@ __global__ void __launch_bounds__(256) dkv_kernel(BParams p)
         }
     }
     if (exists) {
-        store_rowT<NMT>(dk_row, dka, p.scale, kvalid, half);
-        store_rowT<NMT>(dv_row, dva, 1.0f, kvalid, half);
+        store_rowT<NMT>(dk_row, dka, p.scale, kvalid, half, !VARLEN || kvalid);
+        store_rowT<NMT>(dv_row, dva, 1.0f, kvalid, half, !VARLEN || kvalid);
     }
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_bwd_d(const BwdLaunch &a, BParams p)
+template <int D, bool CAUSAL, bool VARLEN>
+hipError_t launch_bwd_v(const BwdLaunch &a, const BParams &p)
 {
     constexpr int NS = 3;
     // dq also writes D (every row of every real block), which dkv reads
-    hipLaunchKernelGGL((dq_kernel<D, NS, CAUSAL>), dim3(p.total), dim3(256), 0, a.stream, p);
+    hipLaunchKernelGGL((dq_kernel<D, NS, CAUSAL, VARLEN>), dim3(p.total), dim3(256), 0, a.stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((dkv_kernel<D, NS, CAUSAL>), dim3(p.total), dim3(256), 0, a.stream, p);
+    hipLaunchKernelGGL((dkv_kernel<D, NS, CAUSAL, VARLEN>), dim3(p.total), dim3(256), 0, a.stream, p);
     return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_d(const BwdLaunch &a, const BParams &p)
+{
+    return a.cu_seqlens ? launch_bwd_v<D, CAUSAL, true>(a, p) : launch_bwd_v<D, CAUSAL, false>(a, p);
 }
 
 } // namespace
@@ -607,13 +660,15 @@ hipError_t launch_bwd_bf16(const BwdLaunch &a)
     p.dout = (const uint16_t *)a.dout;
     p.lse = a.lse;
     p.seqlens = a.seqlens;
+    p.cu = a.cu_seqlens;
+    p.tokens = a.tokens;
     p.dq = (uint16_t *)a.dq;
     p.dk = (uint16_t *)a.dk;
     p.dv = (uint16_t *)a.dv;
     p.delta = a.delta;
     p.heads = a.heads;
     p.n = a.n;
-    p.nblk = a.n / BLK;
+    p.nblk = (a.n + BLK - 1) / BLK;
     p.ngroups = (p.nblk + 3) / 4;
     p.radius = a.radius;
     p.window = a.window;

@@ -10,10 +10,12 @@ namespace bsl {
 struct BwdLaunch {
     const void *q, *k, *v, *o, *dout;
     const float *lse;
-    const int32_t *seqlens;
+    const int32_t *seqlens;    // padded layout; nullptr = every sequence is n long
+    const int32_t *cu_seqlens; // packed layout: batch + 1 offsets (else nullptr)
     void *dq, *dk, *dv;
-    float *delta; // caller's workspace, [batch][heads][n]
+    float *delta; // caller's workspace, [batch][heads][n] (packed: [heads][tokens])
     int32_t batch, heads, n, head_dim, radius;
+    int32_t tokens; // packed layout: rows in the buffers (n: the longest sequence)
     int32_t window; // 0: block band; >= 1: token window (radius = ceil(window / 32))
     bool causal;
     float scale;

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define BSL_VERSION 10500 /* major * 10000 + minor * 100 + patch */
+#define BSL_VERSION 10600 /* major * 10000 + minor * 100 + patch */
 
 typedef enum bsl_status {
     BSL_OK = 0,
@@ -197,6 +197,27 @@ bsl_status bsl_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
                         const void *k, const void *v, const void *o, const void *dout,
                         const float *lse, const int32_t *seqlens, void *dq, void *dk, void *dv,
                         float *delta, void *stream);
+
+/* bsl_backward over the packed layout of bsl_forward_varlen: the same
+ * gradients per sequence, each sequence alone, with the rows back to back.
+ *   batch, tokens, max_seqlen, cu_seqlens, stream  as in bsl_forward_varlen
+ *            (the same values it was given).
+ *   q, k, v, o, dout  device bf16 [tokens][heads][head_dim]: the forward's
+ *            inputs and output, and the loss gradient w.r.t. o.
+ *   lse      device float[heads][tokens]: the lse bsl_forward_varlen wrote.
+ *   dq, dk, dv  device bf16 [tokens][heads][head_dim]: only the rows of the
+ *            sequences are written; rows outside every sequence are left as
+ *            they were.
+ *   delta    device float[heads][tokens], the caller's workspace: D on the
+ *            sequences' rows.
+ * Each sequence's gradients equal, bit for bit, those bsl_backward writes for
+ * the same data in the padded layout.  Errors as bsl_backward, with the size
+ * limits of bsl_forward_varlen; batch, tokens or max_seqlen == 0 is a no-op. */
+bsl_status bsl_backward_varlen(const bsl_plan *plan, int32_t batch, int32_t tokens,
+                               int32_t max_seqlen, const void *q, const void *k, const void *v,
+                               const void *o, const void *dout, const float *lse,
+                               const int32_t *cu_seqlens, void *dq, void *dk, void *dv,
+                               float *delta, void *stream);
 
 /* ------------------------------------------------------------------------
  * Fused 2-bit k-mer tokenization: the step that feeds the model's token IDs

@@ -94,6 +94,11 @@ def test_null_arguments(lib):
     assert lib.bsl_forward_varlen(None, 1, 64, 64, 16, 16, 16, 16, 16, None,
                                   None) == bsl.BSL_E_INVALID
     assert "plan" in bsl.bsl_last_error()
+    assert lib.bsl_backward(None, 1, 32, 16, 16, 16, 16, 16, 16, None, 16, 16, 16, 16,
+                            None) == bsl.BSL_E_INVALID
+    assert lib.bsl_backward_varlen(None, 1, 64, 64, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16,
+                                   None) == bsl.BSL_E_INVALID
+    assert "plan" in bsl.bsl_last_error()
     assert lib.bsl_destroy(None) == bsl.BSL_OK
 
 

@@ -228,3 +228,70 @@ def test_backward_rejects_bad_arguments():
                          *[torch.zeros_like(tf) for _ in range(3)], delta)
     assert e.value.status == bsl.BSL_E_UNSUPPORTED
     pf.close()
+
+
+# ------------------------------------------------------- packed layout backward
+
+def _pack(x, lens, slack):
+    """[batch, heads, n, d] (rows t < lens[b]) -> [tokens + slack, heads, d], NaN slack rows."""
+    parts = [x[b, :, :int(L)].transpose(1, 0, 2) for b, L in enumerate(lens)]
+    parts.append(np.full((slack, x.shape[1], x.shape[3]), np.nan, dtype=x.dtype))
+    return np.ascontiguousarray(np.concatenate(parts, axis=0))
+
+
+PACKED_CASES = [
+    # heads, n, d, radius, causal, window, lens
+    (2, 256, 64, 1, False, 0, [256, 0, 1, 31, 33, 150]),
+    (2, 256, 128, 2, True, 0, [200, 256, 61]),
+    (3, 224, 64, 0, False, 40, [224, 100, 7]),
+    (2, 320, 128, 1, False, 0, [320, 289]),
+]
+
+
+@pytest.mark.parametrize("case", PACKED_CASES)
+def test_backward_packed_layout(case):
+    """bsl_backward_varlen: per sequence the same bits as bsl_backward on the
+    padded layout, within the bar of the oracle, and rows outside every
+    sequence (NaN slack at the end) left untouched."""
+    heads, n, dd, radius, causal, window, lens = case
+    say(f"[backward] packed h{heads} n{n} d{dd} R{radius} causal{int(causal)} W{window} {lens}")
+    lens = np.array(lens, np.int32)
+    d = _case(len(lens), heads, n, dd, radius, causal, lens, seed=dd + radius + 3 * window + 1)
+    padded = _gpu_backward(d, heads, dd, radius, causal, window=window)
+    slack = 5
+    q, k, v, g = (dev(_pack(d[x], lens, slack), "bf16") for x in ("q", "k", "v", "dout"))
+    tokens = q.shape[0]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cu_d = lens_dev(cu)
+    plan = bsl.Plan(head_dim=dd, heads=heads, radius=radius, causal=causal, window=window)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((heads, tokens), float("nan"), dtype=torch.float32, device="cuda")
+    plan.forward_varlen(q, k, v, cu_d, int(lens.max()), o=o, lse=lse)
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    delta = torch.full((heads, tokens), float("nan"), dtype=torch.float32, device="cuda")
+    plan.backward_varlen(q, k, v, o, g, lse, cu_d, int(lens.max()), dq=dq, dk=dk, dv=dv,
+                         delta=delta)
+    torch.cuda.synchronize()
+    plan.close()
+    got = dict(dq=host(dq), dk=host(dk), dv=host(dv))
+    ref = oracle.backward(d["q"], d["k"], d["v"], d["dout"], lens, 32, radius, causal,
+                          window=window if window else None)
+    covered = np.zeros(tokens, bool)
+    for name, r in zip(("dq", "dk", "dv"), ref):
+        unpacked = np.zeros_like(padded[name])
+        for b, L in enumerate(lens):
+            L = int(L)
+            rows = got[name][cu[b]:cu[b] + L].transpose(1, 0, 2)
+            unpacked[b, :, :L] = rows
+            covered[cu[b]:cu[b] + L] = True
+            assert np.array_equal(rows.view(np.uint32) >> 16,
+                                  padded[name][b, :, :L].view(np.uint32) >> 16), \
+                f"{name}: sequence {b} differs from the padded layout"
+        _compare(name, unpacked, r, lens)
+        assert np.all(np.isnan(got[name][~covered])), f"{name}: rows outside the sequences written"
+    dl = delta.cpu().numpy()
+    assert np.all(np.isnan(dl[:, ~covered]))
+    for b, L in enumerate(lens):
+        L = int(L)
+        assert np.array_equal(dl[:, cu[b]:cu[b] + L].view(np.uint32),
+                              padded["delta"][b, :, :L].view(np.uint32))
