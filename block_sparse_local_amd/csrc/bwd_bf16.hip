@@ -263,7 +263,13 @@ __global__ void __launch_bounds__(256) dq_kernel(BParams p)
     const int col = lane & 31, half = lane >> 5;
 
     const int g = xcd_contiguous((int)blockIdx.x, p.total);
-    const int grp = g % p.ngroups, bh = g / p.ngroups, b = bh / p.heads, h = bh % p.heads;
+    // packed layout with 128-byte head pieces (D 64): the heads of a group run
+    // consecutively, so neighbouring workgroups read whole token rows
+    constexpr bool HEADS_FASTEST = VARLEN && D * 2 < 256;
+    const int bh = g / p.ngroups;
+    const int grp = HEADS_FASTEST ? (g / p.heads) % p.ngroups : g % p.ngroups;
+    const int b = HEADS_FASTEST ? g / p.heads / p.ngroups : bh / p.heads;
+    const int h = HEADS_FASTEST ? g % p.heads : bh % p.heads;
     const BSeq<D, VARLEN> sq(p, b, h);
     const int len = sq.len;
     const int nb = (len + BLK - 1) / BLK;
@@ -445,7 +451,13 @@ __global__ void __launch_bounds__(256) dkv_kernel(BParams p)
     const int col = lane & 31, half = lane >> 5;
 
     const int g = xcd_contiguous((int)blockIdx.x, p.total);
-    const int grp = g % p.ngroups, bh = g / p.ngroups, b = bh / p.heads, h = bh % p.heads;
+    // packed layout with 128-byte head pieces (D 64): the heads of a group run
+    // consecutively, so neighbouring workgroups read whole token rows
+    constexpr bool HEADS_FASTEST = VARLEN && D * 2 < 256;
+    const int bh = g / p.ngroups;
+    const int grp = HEADS_FASTEST ? (g / p.heads) % p.ngroups : g % p.ngroups;
+    const int b = HEADS_FASTEST ? g / p.heads / p.ngroups : bh / p.heads;
+    const int h = HEADS_FASTEST ? g % p.heads : bh % p.heads;
     const BSeq<D, VARLEN> sq(p, b, h);
     const int len = sq.len;
     const int nb = (len + BLK - 1) / BLK;
