@@ -193,11 +193,9 @@ bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
     if (!plan)
         return fail(BSL_E_INVALID, "plan is NULL");
     const bsl_desc &d = plan->desc;
-    if (d.dtype != BSL_BF16)
-        return fail(BSL_E_UNSUPPORTED, "the backward pass is built for bf16 plans only");
-    if (d.head_dim != 64 && d.head_dim != 128)
-        return fail(BSL_E_UNSUPPORTED, "the backward pass supports head_dim 64 and 128 (got %d)",
-                    d.head_dim);
+    if (d.dtype == BSL_BF16 && d.head_dim != 64 && d.head_dim != 128)
+        return fail(BSL_E_UNSUPPORTED,
+                    "the bf16 backward pass supports head_dim 64 and 128 (got %d)", d.head_dim);
     if (batch < 0 || n < 0)
         return fail(BSL_E_INVALID, "batch (%d) and n (%d) must be >= 0", batch, n);
     if (n % d.block_size != 0)
@@ -227,7 +225,7 @@ bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
     if ((long long)batch * d.heads * nblk > 0x7fffffffLL ||
         (long long)batch * d.heads * n > 0x7fffffffLL)
         return fail(BSL_E_INVALID, "batch * heads * n exceeds 2^31 - 1");
-    const size_t tb = (size_t)elems * 2;                           // one bf16 tensor
+    const size_t tb = (size_t)elems * (d.dtype == BSL_BF16 ? 2 : 4); // one tensor
     const size_t rb = (size_t)batch * d.heads * (size_t)n * 4;     // one float row vector
     const size_t in_bytes[] = {tb, tb, tb, tb, tb, rb};
     const size_t out_bytes[] = {tb, tb, tb, rb};
@@ -269,7 +267,7 @@ bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
     a.causal = d.causal != 0;
     a.scale = plan->scale;
     a.stream = (hipStream_t)stream;
-    const hipError_t e = bsl::launch_bwd_bf16(a);
+    const hipError_t e = d.dtype == BSL_BF16 ? bsl::launch_bwd_bf16(a) : bsl::launch_bwd_f32(a);
     if (e != hipSuccess)
         return fail(BSL_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return BSL_OK;
@@ -284,11 +282,9 @@ bsl_status run_backward_varlen(const bsl_plan *plan, int32_t batch, int32_t toke
     if (!plan)
         return fail(BSL_E_INVALID, "plan is NULL");
     const bsl_desc &d = plan->desc;
-    if (d.dtype != BSL_BF16)
-        return fail(BSL_E_UNSUPPORTED, "the backward pass is built for bf16 plans only");
-    if (d.head_dim != 64 && d.head_dim != 128)
-        return fail(BSL_E_UNSUPPORTED, "the backward pass supports head_dim 64 and 128 (got %d)",
-                    d.head_dim);
+    if (d.dtype == BSL_BF16 && d.head_dim != 64 && d.head_dim != 128)
+        return fail(BSL_E_UNSUPPORTED,
+                    "the bf16 backward pass supports head_dim 64 and 128 (got %d)", d.head_dim);
     if (batch < 0 || tokens < 0 || max_seqlen < 0)
         return fail(BSL_E_INVALID, "batch (%d), tokens (%d) and max_seqlen (%d) must be >= 0",
                     batch, tokens, max_seqlen);
@@ -319,7 +315,7 @@ bsl_status run_backward_varlen(const bsl_plan *plan, int32_t batch, int32_t toke
         (long long)d.heads * tokens > 0x7fffffffLL)
         return fail(BSL_E_INVALID, "batch * heads * ceil(max_seqlen / 32) or heads * tokens "
                                    "exceeds 2^31 - 1");
-    const size_t tb = (size_t)elems * 2;                          // one bf16 tensor
+    const size_t tb = (size_t)elems * (d.dtype == BSL_BF16 ? 2 : 4); // one tensor
     const size_t rb = (size_t)d.heads * (size_t)tokens * 4;       // one float row vector
     const size_t in_bytes[] = {tb, tb, tb, tb, tb, rb};
     const size_t out_bytes[] = {tb, tb, tb, rb};
@@ -361,7 +357,7 @@ bsl_status run_backward_varlen(const bsl_plan *plan, int32_t batch, int32_t toke
     a.causal = d.causal != 0;
     a.scale = plan->scale;
     a.stream = (hipStream_t)stream;
-    const hipError_t e = bsl::launch_bwd_bf16(a);
+    const hipError_t e = d.dtype == BSL_BF16 ? bsl::launch_bwd_bf16(a) : bsl::launch_bwd_f32(a);
     if (e != hipSuccess)
         return fail(BSL_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return BSL_OK;

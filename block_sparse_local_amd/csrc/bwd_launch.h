@@ -23,5 +23,6 @@ struct BwdLaunch {
 };
 
 hipError_t launch_bwd_bf16(const BwdLaunch &a);
+hipError_t launch_bwd_f32(const BwdLaunch &a);
 
 } // namespace bsl

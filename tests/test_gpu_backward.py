@@ -26,10 +26,11 @@ pytestmark = pytest.mark.gpu
 MAX_TOL, MEAN_TOL = 2e-2, 2e-3
 
 
-def _gpu_backward(d, heads, dd, radius, causal, window=0):
-    q, k, v, g = (dev(d[x], "bf16") for x in ("q", "k", "v", "dout"))
+def _gpu_backward(d, heads, dd, radius, causal, window=0, dtype="bf16"):
+    q, k, v, g = (dev(d[x], dtype) for x in ("q", "k", "v", "dout"))
     sl = lens_dev(d["seqlens"])
-    plan = bsl.Plan(head_dim=dd, heads=heads, radius=radius, causal=causal, window=window)
+    plan = bsl.Plan(head_dim=dd, heads=heads, radius=radius, causal=causal, window=window,
+                    dtype=dtype)
     o = torch.full_like(q, float("nan"))
     lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
     plan.forward(q, k, v, sl, o=o, lse=lse)
@@ -42,8 +43,10 @@ def _gpu_backward(d, heads, dd, radius, causal, window=0):
     return out
 
 
-def _compare(name, got, ref, lens):
+def _compare(name, got, ref, lens, max_tol=None, mean_tol=None):
     """Valid rows within the bar, padded rows exactly zero."""
+    max_tol = MAX_TOL if max_tol is None else max_tol
+    mean_tol = MEAN_TOL if mean_tol is None else mean_tol
     errs, refs = [], []
     for b, L in enumerate(lens):
         L = int(L)
@@ -58,8 +61,8 @@ def _compare(name, got, ref, lens):
     s = max(1.0, float(np.sqrt(np.mean(r * r))))
     say(f"  {name}: max-abs {e.max():.3e} mean-abs {e.mean():.3e} (ref rms {s:.3g}, "
         f"max |ref| {np.abs(r).max():.3g})")
-    assert e.max() <= MAX_TOL * s, f"{name}: max-abs {e.max()} > {MAX_TOL * s}"
-    assert e.mean() <= MEAN_TOL * s, f"{name}: mean-abs {e.mean()} > {MEAN_TOL * s}"
+    assert e.max() <= max_tol * s, f"{name}: max-abs {e.max()} > {max_tol * s}"
+    assert e.mean() <= mean_tol * s, f"{name}: mean-abs {e.mean()} > {mean_tol * s}"
 
 
 def _case(batch, heads, n, dd, radius, causal, lens, seed, sigma=1.0):
@@ -223,10 +226,10 @@ def test_backward_rejects_bad_arguments():
     p32.close()
     pf = bsl.Plan(head_dim=64, heads=1, radius=1, dtype="f32")
     tf = torch.zeros((1, 1, 64, 64), dtype=torch.float32, device="cuda")
-    with pytest.raises(bsl.BslError) as e:
-        bsl.bsl_backward(pf.handle, 1, 64, tf, tf, tf, tf, tf, lse, None,
-                         *[torch.zeros_like(tf) for _ in range(3)], delta)
-    assert e.value.status == bsl.BSL_E_UNSUPPORTED
+    with pytest.raises(bsl.BslError) as e:   # fp32 plan: dq aliases q
+        bsl.bsl_backward(pf.handle, 1, 64, tf, tf, tf, tf, tf, lse, None, tf,
+                         torch.zeros_like(tf), torch.zeros_like(tf), delta)
+    assert e.value.status == bsl.BSL_E_INVALID
     pf.close()
 
 
@@ -295,3 +298,70 @@ def test_backward_packed_layout(case):
         L = int(L)
         assert np.array_equal(dl[:, cu[b]:cu[b] + L].view(np.uint32),
                               padded["delta"][b, :, :L].view(np.uint32))
+
+
+# ------------------------------------------------------------ fp32 backward
+
+# fp32 throughout: unit roundoff 2^-24, sums of at most (2R+1) 32 terms and
+# the hardware 2^x (about 1 ulp), so errors stay near 1e-6 of the gradient's
+# size (measured: max-abs 1.4e-6, mean-abs 5e-8); the bar is the fp32 forward's
+# 1e-5, in units of the gradient's size.
+F32_MAX, F32_MEAN = 1e-5, 1e-6
+
+F32_CASES = [
+    # heads, n, d, radius, causal, window, lens
+    (2, 256, 32, 1, False, 0, [256, 150]),
+    (2, 256, 64, 2, True, 0, [256, 61]),
+    (1, 192, 128, 1, False, 0, [192, 0, 33]),
+    (2, 224, 64, 0, False, 40, [224, 1, 100]),
+    (1, 96, 32, 3, True, 0, [96]),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES)
+def test_backward_f32(case):
+    heads, n, dd, radius, causal, window, lens = case
+    say(f"[backward] fp32 h{heads} n{n} d{dd} R{radius} causal{int(causal)} W{window} {lens}")
+    lens_a = np.array(lens, np.int32)
+    q, k, v, g = inputs.draw(dd + radius + window, 94, len(lens), heads, n, dd, 1.0, False,
+                             lens_a, poison=True, tensors=4)
+    d = dict(q=q, k=k, v=v, dout=g, seqlens=lens_a, n=n)
+    res = _gpu_backward(d, heads, dd, radius, causal, window=window, dtype="f32")
+    ref = oracle.backward(q, k, v, g, lens_a, 32, radius, causal,
+                          window=window if window else None)
+    for name, r in zip(("dq", "dk", "dv"), ref):
+        _compare(name, res[name], r, lens_a, F32_MAX, F32_MEAN)
+    for b, L in enumerate(lens_a):
+        assert np.all(res["delta"][b, :, L:] == 0.0)
+
+
+def test_backward_f32_packed_layout():
+    heads, n, dd = 2, 160, 64
+    lens = np.array([160, 0, 1, 90], np.int32)
+    q, k, v, g = inputs.draw(7, 95, len(lens), heads, n, dd, 1.0, False, lens, poison=True,
+                             tensors=4)
+    d = dict(q=q, k=k, v=v, dout=g, seqlens=lens, n=n)
+    padded = _gpu_backward(d, heads, dd, 1, False, dtype="f32")
+    qp, kp, vp, gp = (dev(_pack(d[x], lens, 3), "f32") for x in ("q", "k", "v", "dout"))
+    tokens = qp.shape[0]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cu_d = lens_dev(cu)
+    plan = bsl.Plan(head_dim=dd, heads=heads, radius=1, dtype="f32")
+    o = torch.full_like(qp, float("nan"))
+    lse = torch.full((heads, tokens), float("nan"), dtype=torch.float32, device="cuda")
+    plan.forward_varlen(qp, kp, vp, cu_d, int(lens.max()), o=o, lse=lse)
+    dq, dk, dv = (torch.full_like(qp, float("nan")) for _ in range(3))
+    delta = torch.full((heads, tokens), float("nan"), dtype=torch.float32, device="cuda")
+    plan.backward_varlen(qp, kp, vp, o, gp, lse, cu_d, int(lens.max()), dq=dq, dk=dk, dv=dv,
+                         delta=delta)
+    torch.cuda.synchronize()
+    plan.close()
+    got = dict(dq=host(dq), dk=host(dk), dv=host(dv))
+    covered = np.zeros(tokens, bool)
+    for name in ("dq", "dk", "dv"):
+        for b, L in enumerate(lens):
+            L = int(L)
+            covered[cu[b]:cu[b] + L] = True
+            rows = got[name][cu[b]:cu[b] + L].transpose(1, 0, 2)
+            assert np.array_equal(rows.view(np.uint32), padded[name][b, :, :L].view(np.uint32))
+        assert np.all(np.isnan(got[name][~covered]))
