@@ -25,7 +25,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbsl.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["fwd_bf16.hip", "fwd_f32.hip", "bwd_bf16.hip", "bwd_f32.hip", "kmer.hip", "check.hip",
+SOURCES = ["fwd_bf16.hip", "fwd_f32.hip", "bwd_bf16.hip", "bwd_valu.hip", "kmer.hip", "check.hip",
            "bsl_api.cpp"]
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror", f"--offload-arch={ARCH}",

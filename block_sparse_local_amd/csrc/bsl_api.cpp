@@ -193,9 +193,6 @@ bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
     if (!plan)
         return fail(BSL_E_INVALID, "plan is NULL");
     const bsl_desc &d = plan->desc;
-    if (d.dtype == BSL_BF16 && d.head_dim != 64 && d.head_dim != 128)
-        return fail(BSL_E_UNSUPPORTED,
-                    "the bf16 backward pass supports head_dim 64 and 128 (got %d)", d.head_dim);
     if (batch < 0 || n < 0)
         return fail(BSL_E_INVALID, "batch (%d) and n (%d) must be >= 0", batch, n);
     if (n % d.block_size != 0)
@@ -267,7 +264,10 @@ bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
     a.causal = d.causal != 0;
     a.scale = plan->scale;
     a.stream = (hipStream_t)stream;
-    const hipError_t e = d.dtype == BSL_BF16 ? bsl::launch_bwd_bf16(a) : bsl::launch_bwd_f32(a);
+    // bf16 at head_dim 64 and 128 on the matrix cores; the rest on the vector ALUs
+    const hipError_t e = d.dtype == BSL_BF16 && d.head_dim != 32
+                             ? bsl::launch_bwd_bf16(a)
+                             : bsl::launch_bwd_valu(a, d.dtype == BSL_BF16);
     if (e != hipSuccess)
         return fail(BSL_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return BSL_OK;
@@ -282,9 +282,6 @@ bsl_status run_backward_varlen(const bsl_plan *plan, int32_t batch, int32_t toke
     if (!plan)
         return fail(BSL_E_INVALID, "plan is NULL");
     const bsl_desc &d = plan->desc;
-    if (d.dtype == BSL_BF16 && d.head_dim != 64 && d.head_dim != 128)
-        return fail(BSL_E_UNSUPPORTED,
-                    "the bf16 backward pass supports head_dim 64 and 128 (got %d)", d.head_dim);
     if (batch < 0 || tokens < 0 || max_seqlen < 0)
         return fail(BSL_E_INVALID, "batch (%d), tokens (%d) and max_seqlen (%d) must be >= 0",
                     batch, tokens, max_seqlen);
@@ -357,7 +354,10 @@ bsl_status run_backward_varlen(const bsl_plan *plan, int32_t batch, int32_t toke
     a.causal = d.causal != 0;
     a.scale = plan->scale;
     a.stream = (hipStream_t)stream;
-    const hipError_t e = d.dtype == BSL_BF16 ? bsl::launch_bwd_bf16(a) : bsl::launch_bwd_f32(a);
+    // bf16 at head_dim 64 and 128 on the matrix cores; the rest on the vector ALUs
+    const hipError_t e = d.dtype == BSL_BF16 && d.head_dim != 32
+                             ? bsl::launch_bwd_bf16(a)
+                             : bsl::launch_bwd_valu(a, d.dtype == BSL_BF16);
     if (e != hipSuccess)
         return fail(BSL_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return BSL_OK;

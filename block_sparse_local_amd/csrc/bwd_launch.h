@@ -23,6 +23,7 @@ struct BwdLaunch {
 };
 
 hipError_t launch_bwd_bf16(const BwdLaunch &a);
-hipError_t launch_bwd_f32(const BwdLaunch &a);
+// The vector-ALU backward: fp32 plans, and bf16 plans at head_dim 32 (bf16 = true).
+hipError_t launch_bwd_valu(const BwdLaunch &a, bool bf16);
 
 } // namespace bsl

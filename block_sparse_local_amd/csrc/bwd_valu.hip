@@ -1,10 +1,13 @@
-// bwd_f32.hip -- backward pass of the banded block-sparse attention, fp32, gfx950.
+// bwd_valu.hip -- backward pass of the banded block-sparse attention on the
+// vector ALUs, gfx950.
 //
 // The gradients bwd_bf16.hip computes (NucleoByte project page, section 3,
 // "Custom Backpropagation": D_t = sum_c dO_tc O_tc, dS_ts = P_ts (dO_t . V_s -
 // D_t), then dV = P^T dO, dQ = scale dS K, dK = scale dS^T Q), with every
 // product and sum in fp32 on the vector ALUs, as fwd_f32.hip does for the
-// forward: the path for fp32 plans and every head size, not the fast one.  P is
+// forward: the path for fp32 plans at every head size and for bf16 plans at
+// head_dim 32 (inputs widened to fp32, gradients rounded once to bf16), not
+// the fast one.  P is
 // recomputed from the scores and the forward's lse; the band, padding, causal
 // and token-window rules are the forward's.
 //
@@ -29,11 +32,26 @@ namespace {
 constexpr int BLK = 32;
 constexpr float LOG2E = 1.4426950408889634f;
 
+// Elements are float or bf16 bits (uint16_t); arithmetic is fp32 either way.
+__device__ __forceinline__ float widen(float x) { return x; }
+__device__ __forceinline__ float widen(uint16_t x)
+{
+    return __builtin_bit_cast(float, (uint32_t)x << 16);
+}
+__device__ __forceinline__ void put(float *p, float x) { *p = x; }
+__device__ __forceinline__ void put(uint16_t *p, float x)
+{
+    *p = __builtin_bit_cast(uint16_t, (__bf16)x); // round to nearest even
+}
+
+template <typename T>
 struct FParams {
-    const float *q, *k, *v, *o, *dout, *lse;
+    const T *q, *k, *v, *o, *dout;
+    const float *lse;
     const int32_t *seqlens; // padded layout: lengths (or nullptr)
     const int32_t *cu;      // packed layout: sequence start offsets, batch + 1 of them
-    float *dq, *dk, *dv, *delta;
+    T *dq, *dk, *dv;
+    float *delta;
     int32_t heads, n, nblk, radius, total, tokens, window;
     float c;     // scale * log2(e)
     float scale;
@@ -46,7 +64,8 @@ template <int D, bool VARLEN>
 struct FSeq {
     size_t base, lbase, rs;
     int len;
-    __device__ __forceinline__ FSeq(const FParams &p, int b, int h)
+    template <typename T>
+    __device__ __forceinline__ FSeq(const FParams<T> &p, int b, int h)
     {
         if (VARLEN) {
             int s0 = p.cu[b], s1 = p.cu[b + 1];
@@ -81,8 +100,8 @@ __device__ __forceinline__ bool kept(int t, int s, int len, bool causal, int win
 }
 
 // ------------------------------------------------------------------- dq
-template <int D, bool CAUSAL, bool VARLEN>
-__global__ void __launch_bounds__(256) dq_f32_kernel(FParams p)
+template <typename T, int D, bool CAUSAL, bool VARLEN>
+__global__ void __launch_bounds__(256) dq_valu_kernel(FParams<T> p)
 {
     constexpr int E = D / 8;
     __shared__ float kl[BLK][D + 1];
@@ -103,9 +122,9 @@ __global__ void __launch_bounds__(256) dq_f32_kernel(FParams p)
     float dpart = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        qv[e] = tvalid ? p.q[row + e * 8 + sub] : 0.0f;
-        gv[e] = tvalid ? p.dout[row + e * 8 + sub] : 0.0f;
-        const float ov = tvalid ? p.o[row + e * 8 + sub] : 0.0f;
+        qv[e] = tvalid ? widen(p.q[row + e * 8 + sub]) : 0.0f;
+        gv[e] = tvalid ? widen(p.dout[row + e * 8 + sub]) : 0.0f;
+        const float ov = tvalid ? widen(p.o[row + e * 8 + sub]) : 0.0f;
         dpart = fmaf(gv[e], ov, dpart);
         acc[e] = 0.0f;
     }
@@ -128,8 +147,8 @@ __global__ void __launch_bounds__(256) dq_f32_kernel(FParams p)
             const int s = j * BLK + kr;
             const bool ok = s < len;
             const size_t src = sq.base + (size_t)(ok ? s : 0) * sq.rs + kc;
-            kl[kr][kc] = ok ? p.k[src] : 0.0f;
-            vl[kr][kc] = ok ? p.v[src] : 0.0f;
+            kl[kr][kc] = ok ? widen(p.k[src]) : 0.0f;
+            vl[kr][kc] = ok ? widen(p.v[src]) : 0.0f;
         }
         __syncthreads();
         for (int c = 0; c < BLK; ++c) {
@@ -154,12 +173,12 @@ __global__ void __launch_bounds__(256) dq_f32_kernel(FParams p)
         return;
 #pragma unroll
     for (int e = 0; e < E; ++e)
-        p.dq[row + e * 8 + sub] = tvalid ? acc[e] * p.scale : 0.0f;
+        put(&p.dq[row + e * 8 + sub], tvalid ? acc[e] * p.scale : 0.0f);
 }
 
 // ------------------------------------------------------------------ dkv
-template <int D, bool CAUSAL, bool VARLEN>
-__global__ void __launch_bounds__(256) dkv_f32_kernel(FParams p)
+template <typename T, int D, bool CAUSAL, bool VARLEN>
+__global__ void __launch_bounds__(256) dkv_valu_kernel(FParams<T> p)
 {
     constexpr int E = D / 8;
     __shared__ float ql[BLK][D + 1];
@@ -180,8 +199,8 @@ __global__ void __launch_bounds__(256) dkv_f32_kernel(FParams p)
     float kv[E], vv[E], dk[E], dv[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        kv[e] = svalid ? p.k[row + e * 8 + sub] : 0.0f;
-        vv[e] = svalid ? p.v[row + e * 8 + sub] : 0.0f;
+        kv[e] = svalid ? widen(p.k[row + e * 8 + sub]) : 0.0f;
+        vv[e] = svalid ? widen(p.v[row + e * 8 + sub]) : 0.0f;
         dk[e] = 0.0f;
         dv[e] = 0.0f;
     }
@@ -200,8 +219,8 @@ __global__ void __launch_bounds__(256) dkv_f32_kernel(FParams p)
             const int t = i * BLK + qr;
             const bool ok = t < len;
             const size_t src = sq.base + (size_t)(ok ? t : 0) * sq.rs + qc;
-            ql[qr][qc] = ok ? p.q[src] : 0.0f;
-            gl[qr][qc] = ok ? p.dout[src] : 0.0f;
+            ql[qr][qc] = ok ? widen(p.q[src]) : 0.0f;
+            gl[qr][qc] = ok ? widen(p.dout[src]) : 0.0f;
         }
         if (tid < BLK) {
             const int t = i * BLK + tid;
@@ -234,48 +253,48 @@ __global__ void __launch_bounds__(256) dkv_f32_kernel(FParams p)
         return;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        p.dk[row + e * 8 + sub] = svalid ? dk[e] * p.scale : 0.0f;
-        p.dv[row + e * 8 + sub] = svalid ? dv[e] : 0.0f;
+        put(&p.dk[row + e * 8 + sub], svalid ? dk[e] * p.scale : 0.0f);
+        put(&p.dv[row + e * 8 + sub], svalid ? dv[e] : 0.0f);
     }
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
-hipError_t launch_v(const BwdLaunch &a, const FParams &p)
+template <typename T, int D, bool CAUSAL, bool VARLEN>
+hipError_t launch_v(const BwdLaunch &a, const FParams<T> &p)
 {
     // dq also writes D, which dkv reads
-    hipLaunchKernelGGL((dq_f32_kernel<D, CAUSAL, VARLEN>), dim3(p.total), dim3(256), 0, a.stream, p);
+    hipLaunchKernelGGL((dq_valu_kernel<T, D, CAUSAL, VARLEN>), dim3(p.total), dim3(256), 0,
+                       a.stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((dkv_f32_kernel<D, CAUSAL, VARLEN>), dim3(p.total), dim3(256), 0, a.stream,
-                       p);
+    hipLaunchKernelGGL((dkv_valu_kernel<T, D, CAUSAL, VARLEN>), dim3(p.total), dim3(256), 0,
+                       a.stream, p);
     return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_d(const BwdLaunch &a, const FParams &p)
+template <typename T, int D>
+hipError_t launch_d(const BwdLaunch &a, const FParams<T> &p)
 {
     if (a.cu_seqlens)
-        return a.causal ? launch_v<D, true, true>(a, p) : launch_v<D, false, true>(a, p);
-    return a.causal ? launch_v<D, true, false>(a, p) : launch_v<D, false, false>(a, p);
+        return a.causal ? launch_v<T, D, true, true>(a, p) : launch_v<T, D, false, true>(a, p);
+    return a.causal ? launch_v<T, D, true, false>(a, p) : launch_v<T, D, false, false>(a, p);
 }
 
-} // namespace
-
-hipError_t launch_bwd_f32(const BwdLaunch &a)
+template <typename T>
+hipError_t launch_typed(const BwdLaunch &a)
 {
-    FParams p;
-    p.q = (const float *)a.q;
-    p.k = (const float *)a.k;
-    p.v = (const float *)a.v;
-    p.o = (const float *)a.o;
-    p.dout = (const float *)a.dout;
+    FParams<T> p;
+    p.q = (const T *)a.q;
+    p.k = (const T *)a.k;
+    p.v = (const T *)a.v;
+    p.o = (const T *)a.o;
+    p.dout = (const T *)a.dout;
     p.lse = a.lse;
     p.seqlens = a.seqlens;
     p.cu = a.cu_seqlens;
-    p.dq = (float *)a.dq;
-    p.dk = (float *)a.dk;
-    p.dv = (float *)a.dv;
+    p.dq = (T *)a.dq;
+    p.dk = (T *)a.dk;
+    p.dv = (T *)a.dv;
     p.delta = a.delta;
     p.heads = a.heads;
     p.n = a.n;
@@ -287,11 +306,18 @@ hipError_t launch_bwd_f32(const BwdLaunch &a)
     p.c = a.scale * LOG2E;
     p.scale = a.scale;
     switch (a.head_dim) {
-    case 32: return launch_d<32>(a, p);
-    case 64: return launch_d<64>(a, p);
-    case 128: return launch_d<128>(a, p);
+    case 32: return launch_d<T, 32>(a, p);
+    case 64: return launch_d<T, 64>(a, p);
+    case 128: return launch_d<T, 128>(a, p);
     default: return hipErrorInvalidValue;
     }
+}
+
+} // namespace
+
+hipError_t launch_bwd_valu(const BwdLaunch &a, bool bf16)
+{
+    return bf16 ? launch_typed<uint16_t>(a) : launch_typed<float>(a);
 }
 
 } // namespace bsl

@@ -176,14 +176,13 @@ bsl_status bsl_varlen_offsets(int32_t batch, const int32_t *lengths, int32_t *cu
  * dV of the same loss.  With P the forward's softmax over each row's kept keys,
  *   D_t = sum_c dO_tc O_tc,   dS_ts = P_ts (dO_t . V_s - D_t),
  *   dV = P^T dO,   dQ = scale dS K,   dK = scale dS^T Q,
- * and zero gradient on padded rows and keys.  bf16 plans: head_dim 64 or 128
- * (MFMA kernels); fp32 plans: head_dim 32, 64 or 128 (vector-ALU kernels, fp32
- * throughout).
+ * and zero gradient on padded rows and keys.  bf16 plans at head_dim 64 and
+ * 128 run on MFMA kernels; fp32 plans, and bf16 plans at head_dim 32, on
+ * vector-ALU kernels (fp32 arithmetic; bf16 gradients rounded once).
  *   batch, n, seqlens, stream  as in bsl_forward (the same values it was given).
  *   q, k, v  the forward's inputs; o its output, exactly as bsl_forward wrote it.
  *   dout     device [batch][heads][n][head_dim] in the plan's dtype: the loss
- *            gradient w.r.t. o.
- *            Rows past a sequence's length are ignored.
+ *            gradient w.r.t. o.  Rows past a sequence's length are ignored.
  *   lse      device float[batch][heads][n]: the lse bsl_forward wrote.
  *   dq, dk, dv  device, same shape and dtype as q; every element is written.
  *   delta    device float[batch][heads][n], a workspace the caller owns: the
@@ -191,9 +190,9 @@ bsl_status bsl_varlen_offsets(int32_t batch, const int32_t *lengths, int32_t *cu
  *            allocates nothing.
  * All tensors 16-byte aligned.  dq, dk, dv and delta must not overlap each
  * other or any input.  A plan with a token window differentiates the window
- * forward.  Returns BSL_E_UNSUPPORTED for a bf16 plan with head_dim 32,
- * BSL_E_INVALID for the argument errors bsl_forward rejects, a NULL pointer,
- * misalignment or overlap, and BSL_E_DEVICE if a launch fails.
+ * forward.  Returns BSL_E_INVALID for the argument errors bsl_forward
+ * rejects, a NULL pointer, misalignment or overlap, and BSL_E_DEVICE if a
+ * launch fails.
  * Nothing is written when an argument error is returned. */
 bsl_status bsl_backward(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
                         const void *k, const void *v, const void *o, const void *dout,
