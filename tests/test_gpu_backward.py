@@ -370,3 +370,28 @@ def test_backward_f32_packed_layout():
             rows = got[name][cu[b]:cu[b] + L].transpose(1, 0, 2)
             assert np.array_equal(rows.view(np.uint32), padded[name][b, :, :L].view(np.uint32))
         assert np.all(np.isnan(got[name][~covered]))
+
+
+def test_backward_packed_offsets_are_clamped():
+    """Offsets out of order or past the buffer are clamped on the device, as in
+    the forward: with offsets [0, 60, 40, 1000, 2000] over 100 rows the
+    sequences become [0, 60), an empty one, [40, 100) and an empty one, so the
+    call succeeds and every row it writes (here all 100) is finite."""
+    heads, dd, tokens = 2, 64, 100
+    rng = np.random.default_rng(5)
+    q, k, v, g = (torch.from_numpy(inputs.bf16_bits(
+        rng.standard_normal((tokens, heads, dd)).astype(np.float32)).view(np.int16))
+        .view(torch.bfloat16).cuda() for _ in range(4))
+    cu = lens_dev(np.array([0, 60, 40, 1000, 2000], np.int32))
+    plan = bsl.Plan(head_dim=dd, heads=heads, radius=1)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((heads, tokens), float("nan"), dtype=torch.float32, device="cuda")
+    plan.forward_varlen(q, k, v, cu, 64, o=o, lse=lse)
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    delta = torch.full((heads, tokens), float("nan"), dtype=torch.float32, device="cuda")
+    plan.backward_varlen(q, k, v, o, g, lse, cu, 64, dq=dq, dk=dk, dv=dv, delta=delta)
+    torch.cuda.synchronize()
+    plan.close()
+    for t in (dq, dk, dv):
+        assert np.all(np.isfinite(host(t))), "every row lies in a clamped sequence"
+    assert np.all(np.isfinite(delta.cpu().numpy()))
