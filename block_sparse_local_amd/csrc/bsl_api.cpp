@@ -185,23 +185,12 @@ bsl_status run_varlen(const bsl_plan *plan, int32_t batch, int32_t tokens, int32
     return BSL_OK;
 }
 
-bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
-                        const void *k, const void *v, const void *o, const void *dout,
-                        const float *lse, const int32_t *seqlens, void *dq, void *dk, void *dv,
-                        float *delta, void *stream)
+// Pointer, alignment, overlap and device checks shared by the two backward
+// entry points: ins = {q, k, v, o, dout, lse}, outs = {dq, dk, dv, delta}; tb
+// bytes per tensor, rb per row vector (lse, delta).  BSL_OK when all pass.
+bsl_status check_bwd_buffers(const bsl_plan *plan, const void *const (&ins)[6],
+                             void *const (&outs)[4], size_t tb, size_t rb, bool sizes_known)
 {
-    if (!plan)
-        return fail(BSL_E_INVALID, "plan is NULL");
-    const bsl_desc &d = plan->desc;
-    if (batch < 0 || n < 0)
-        return fail(BSL_E_INVALID, "batch (%d) and n (%d) must be >= 0", batch, n);
-    if (n % d.block_size != 0)
-        return fail(BSL_E_INVALID, "n (%d) is not a multiple of the block size %d", n,
-                    d.block_size);
-    if (batch == 0 || n == 0)
-        return BSL_OK;
-    const void *ins[] = {q, k, v, o, dout, lse};
-    void *outs[] = {dq, dk, dv, delta};
     for (const void *x : ins)
         if (!x)
             return fail(BSL_E_INVALID, "q, k, v, o, dout and lse must be non-NULL device pointers");
@@ -214,16 +203,8 @@ bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
     for (const void *x : outs)
         if (!aligned16(x))
             return fail(BSL_E_INVALID, "every tensor must be 16-byte aligned");
-    const long double elems = (long double)batch * d.heads * (long double)n * d.head_dim;
-    if (elems > 9.0e18L)
-        return fail(BSL_E_INVALID, "tensor of %d x %d x %d x %d elements is too large", batch,
-                    d.heads, n, d.head_dim);
-    const long long nblk = n / d.block_size;
-    if ((long long)batch * d.heads * nblk > 0x7fffffffLL ||
-        (long long)batch * d.heads * n > 0x7fffffffLL)
-        return fail(BSL_E_INVALID, "batch * heads * n exceeds 2^31 - 1");
-    const size_t tb = (size_t)elems * (d.dtype == BSL_BF16 ? 2 : 4); // one tensor
-    const size_t rb = (size_t)batch * d.heads * (size_t)n * 4;     // one float row vector
+    if (!sizes_known)
+        return BSL_OK;
     const size_t in_bytes[] = {tb, tb, tb, tb, tb, rb};
     const size_t out_bytes[] = {tb, tb, tb, rb};
     for (int a = 0; a < 4; ++a) {
@@ -240,6 +221,40 @@ bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
     if (dev != plan->device)
         return fail(BSL_E_INVALID, "current device %d is not the plan's device %d", dev,
                     plan->device);
+    return BSL_OK;
+}
+
+bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
+                        const void *k, const void *v, const void *o, const void *dout,
+                        const float *lse, const int32_t *seqlens, void *dq, void *dk, void *dv,
+                        float *delta, void *stream)
+{
+    if (!plan)
+        return fail(BSL_E_INVALID, "plan is NULL");
+    const bsl_desc &d = plan->desc;
+    if (batch < 0 || n < 0)
+        return fail(BSL_E_INVALID, "batch (%d) and n (%d) must be >= 0", batch, n);
+    if (n % d.block_size != 0)
+        return fail(BSL_E_INVALID, "n (%d) is not a multiple of the block size %d", n,
+                    d.block_size);
+    if (batch == 0 || n == 0)
+        return BSL_OK;
+    const void *const ins[] = {q, k, v, o, dout, lse};
+    void *const outs[] = {dq, dk, dv, delta};
+    if (const bsl_status st = check_bwd_buffers(plan, ins, outs, 0, 0, false))
+        return st;
+    const long double elems = (long double)batch * d.heads * (long double)n * d.head_dim;
+    if (elems > 9.0e18L)
+        return fail(BSL_E_INVALID, "tensor of %d x %d x %d x %d elements is too large", batch,
+                    d.heads, n, d.head_dim);
+    const long long nblk = n / d.block_size;
+    if ((long long)batch * d.heads * nblk > 0x7fffffffLL ||
+        (long long)batch * d.heads * n > 0x7fffffffLL)
+        return fail(BSL_E_INVALID, "batch * heads * n exceeds 2^31 - 1");
+    const size_t tb = (size_t)elems * (d.dtype == BSL_BF16 ? 2 : 4); // one tensor
+    const size_t rb = (size_t)batch * d.heads * (size_t)n * 4;     // one float row vector
+    if (const bsl_status st = check_bwd_buffers(plan, ins, outs, tb, rb, true))
+        return st;
 
     bsl::BwdLaunch a;
     a.q = q;
@@ -289,20 +304,10 @@ bsl_status run_backward_varlen(const bsl_plan *plan, int32_t batch, int32_t toke
         return BSL_OK;
     if (!cu_seqlens)
         return fail(BSL_E_INVALID, "cu_seqlens must be a non-NULL device pointer");
-    const void *ins[] = {q, k, v, o, dout, lse};
-    void *outs[] = {dq, dk, dv, delta};
-    for (const void *x : ins)
-        if (!x)
-            return fail(BSL_E_INVALID, "q, k, v, o, dout and lse must be non-NULL device pointers");
-    for (const void *x : outs)
-        if (!x)
-            return fail(BSL_E_INVALID, "dq, dk, dv and delta must be non-NULL device pointers");
-    for (const void *x : ins)
-        if (!aligned16(x))
-            return fail(BSL_E_INVALID, "every tensor must be 16-byte aligned");
-    for (const void *x : outs)
-        if (!aligned16(x))
-            return fail(BSL_E_INVALID, "every tensor must be 16-byte aligned");
+    const void *const ins[] = {q, k, v, o, dout, lse};
+    void *const outs[] = {dq, dk, dv, delta};
+    if (const bsl_status st = check_bwd_buffers(plan, ins, outs, 0, 0, false))
+        return st;
     const long double elems = (long double)tokens * d.heads * (long double)d.head_dim;
     if (elems > 9.0e18L)
         return fail(BSL_E_INVALID, "tensor of %d x %d x %d elements is too large", tokens,
@@ -314,22 +319,8 @@ bsl_status run_backward_varlen(const bsl_plan *plan, int32_t batch, int32_t toke
                                    "exceeds 2^31 - 1");
     const size_t tb = (size_t)elems * (d.dtype == BSL_BF16 ? 2 : 4); // one tensor
     const size_t rb = (size_t)d.heads * (size_t)tokens * 4;       // one float row vector
-    const size_t in_bytes[] = {tb, tb, tb, tb, tb, rb};
-    const size_t out_bytes[] = {tb, tb, tb, rb};
-    for (int a = 0; a < 4; ++a) {
-        for (int b = 0; b < 6; ++b)
-            if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b]))
-                return fail(BSL_E_INVALID, "dq, dk, dv and delta must not overlap any input");
-        for (int b = a + 1; b < 4; ++b)
-            if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b]))
-                return fail(BSL_E_INVALID, "dq, dk, dv and delta must not overlap each other");
-    }
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return fail(BSL_E_DEVICE, "hipGetDevice failed");
-    if (dev != plan->device)
-        return fail(BSL_E_INVALID, "current device %d is not the plan's device %d", dev,
-                    plan->device);
+    if (const bsl_status st = check_bwd_buffers(plan, ins, outs, tb, rb, true))
+        return st;
 
     bsl::BwdLaunch a;
     a.q = q;
