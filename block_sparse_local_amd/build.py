@@ -56,7 +56,7 @@ def _compile(src, obj, extra=(), vgpr_form=True):
     if is_hip:
         cmd += [*DEVICE_ONLY, *(VGPR_FORM if vgpr_form else []), "-x", "hip"]
     else:
-        cmd += ["-x", "hip"]  # host-only file, but compiled by the same driver
+        cmd += ["-x", "hip"]  # host-only file, compiled by hipcc like the kernels
     cmd += [*extra, "-c", src, "-o", obj]
     subprocess.run(cmd, check=True)
 

@@ -503,7 +503,7 @@ const char *bsl_status_string(bsl_status s)
     switch (s) {
     case BSL_OK: return "BSL_OK";
     case BSL_E_INVALID: return "BSL_E_INVALID: invalid argument";
-    case BSL_E_UNSUPPORTED: return "BSL_E_UNSUPPORTED: not supported by this build or device";
+    case BSL_E_UNSUPPORTED: return "BSL_E_UNSUPPORTED: not supported by this library or device";
     case BSL_E_DEVICE: return "BSL_E_DEVICE: HIP runtime error";
     case BSL_E_NOMEM: return "BSL_E_NOMEM: out of host memory";
     }

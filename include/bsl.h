@@ -50,7 +50,7 @@ extern "C" {
 typedef enum bsl_status {
     BSL_OK = 0,
     BSL_E_INVALID = 1,     /* bad argument: nothing was launched or written */
-    BSL_E_UNSUPPORTED = 2, /* well-formed but outside what this build supports */
+    BSL_E_UNSUPPORTED = 2, /* well-formed but outside what this library supports */
     BSL_E_DEVICE = 3,      /* HIP runtime failure (device query or launch) */
     BSL_E_NOMEM = 4        /* host allocation of a plan failed */
 } bsl_status;
