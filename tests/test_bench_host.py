@@ -156,3 +156,16 @@ def test_account_backward():
     b4 = workload.account_backward(l4, c4.heads, c4.d, c4.radius, c4.causal, c4.dtype)
     assert b4["bound"] == "mfma" and b4["t_mfma"] > b4["t_hbm"]
 
+
+
+@pytest.mark.parametrize("window,causal", [(40, False), (256, True)])
+def test_account_backward_window_matches_the_oracle(window, causal):
+    lens = np.array([700, 129], np.int32)
+    n = 704
+    act = oracle.active_blocks(len(lens), n, 32, 0, causal, lens, window=window)
+    msk = oracle.masks(len(lens), n, 32, 0, causal, lens, act, window=window)
+    bits = int(np.unpackbits(msk.astype("<u4").view(np.uint8)).sum())
+    acc = workload.account_backward(lens, 4, 128, 0, causal, "bf16", window=window)
+    assert acc["useful_pairs"] == bits * 4
+    assert acc["useful_flops"] == 10.0 * 128 * bits * 4
+    assert acc["block_pairs"] == int((act >= 0).sum()) * 4
