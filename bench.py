@@ -20,7 +20,10 @@ steps between two device synchronisations.  Prints one JSON line:
 
 The default workload is the 1.3B-shape long-context case: batch 1, 16 heads,
 131072-row buffer holding a 130000-token sequence, head dim 128, radius 8.
-``--secondary`` also times the million-token case in the same run;
+The million-token case (c5, the other workload with a roofline target) is
+timed in the same run, beside the headline (``--no-secondary`` skips it);
+every timed workload also gets a cold-cache pass (1 GiB written between
+launches, outside the events), reported under ``detail.cold``;
 ``--window W`` also times the chosen workload with a token window of W tokens
 (|t - s| <= W) in place of the block band.
 """
@@ -174,24 +177,34 @@ def time_workload(key, steps, warmup, cold=False, log=print, layout="padded", wi
         call()
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t_begin = time.perf_counter()
-    for s in range(steps):
-        if flush is not None:
-            flush.fill_(float(s))
-        starts[s].record(stream)
-        call()
-        ends[s].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_begin
-    per_launch = np.array([a.elapsed_time(b) * 1e-3 for a, b in zip(starts, ends)])
+    def timed(flush):
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t_begin = time.perf_counter()
+        for s in range(steps):
+            if flush is not None:
+                flush.fill_(float(s))
+            starts[s].record(stream)
+            call()
+            ends[s].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_begin
+        return wall, np.array([a.elapsed_time(b) * 1e-3 for a, b in zip(starts, ends)])
+
+    wall, per_launch = timed(flush)
+    # caches made cold before every launch: 1 GiB written between launches
+    # (outside the events), more than the L2s and the 256 MB Infinity Cache hold
+    if flush is None:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        _, cold_launch = timed(flush)
+    else:
+        cold_launch = per_launch
     plan.close()
     del q, k, v, o, flush
     torch.cuda.empty_cache()
     return dict(key=key, w=w, d=d, acc=acc, wall=wall, per_launch=per_launch, steps=steps,
-                layout=layout, buffer_bytes=buffer_bytes, window=window)
+                layout=layout, buffer_bytes=buffer_bytes, window=window, cold_launch=cold_launch)
 
 
 def copy_bandwidth(reps=10):
@@ -298,11 +311,24 @@ def cpu_baseline_backward(r, target_flops=6.0e11, log=print):
     acc = workload.account_backward(lens, w.heads, w.d, w.radius, w.causal, w.dtype, window)
     log(f"[bench] oracle backward: {w.heads} heads x {L} tokens in {dt:.1f}s")
     return {"value": acc["useful_flops"] / dt / 1e12, "unit": "TFLOP/s",
-            "cores": min(threads, w.heads), "kind": "oracle",
+            "cores": min(threads, w.heads), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"backward of all {w.heads} heads over the first {L} tokens of sequence 0 "
                       f"(one thread per head); {acc['useful_flops'] / 1e9:.1f} useful GFLOP in "
                       f"{dt:.2f}s",
             "seconds": dt}
+
+
+def cpu_model():
+    """The host processor's model name (from /proc/cpuinfo), or the platform's."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
 
 
 def cpu_baseline(r, target_flops=1.0e12, log=print):
@@ -349,6 +375,7 @@ def cpu_baseline(r, target_flops=1.0e12, log=print):
     log(f"[bench] oracle: {len(sel)} (sequence, head, query block) units in {dt:.1f}s "
         f"on {threads} threads")
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{len(sel)} query blocks (of {w.batch * nblk * w.heads} block-heads): "
                       f"{len(sel) // w.heads} evenly spaced blocks x all {w.heads} heads; "
                       f"{flops / 1e9:.1f} useful GFLOP in {dt:.2f}s",
@@ -426,6 +453,7 @@ def cpu_baseline_kmer(d, log=print, target_bytes=2.0e9):
     windows = int(nt.sum())
     log(f"[bench] oracle tokenizer: {nseq} sequences, {windows} windows in {dt:.1f}s")
     return {"value": windows / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"the first {nseq} of {w.batch} sequences ({len(text)} bases, "
                       f"{windows} windows), one thread", "seconds": dt}
 
@@ -444,6 +472,7 @@ def summarize(r, traffic=None):
                 "peak": acc["flops_peak"] / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
+    cold = r.get("cold_launch")
     extra = {
         "useful_tflops": flops / t_step / 1e12,
         "tokens_per_s": acc["tokens"] / t_step,
@@ -460,6 +489,16 @@ def summarize(r, traffic=None):
         "mfma_frac": flops / mean_launch / acc["flops_peak"],
         "roofline_frac": max(acc["t_hbm"], acc["t_mfma"]) / mean_launch,
     }
+    if cold is not None:
+        med = float(np.median(cold))
+        extra["cold"] = {
+            "what": "1 GiB written between launches (outside the events): every launch starts "
+                    "with cold L2s and Infinity Cache",
+            "median_launch_us": med * 1e6, "min_launch_us": float(cold.min()) * 1e6,
+            "p90_launch_us": float(np.percentile(cold, 90)) * 1e6,
+            "useful_tflops": flops / med / 1e12, "tokens_per_s": acc["tokens"] / med,
+            "roofline_frac": max(acc["t_hbm"], acc["t_mfma"]) / med,
+        }
     return t_step, roof, extra
 
 
@@ -477,8 +516,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
-    ap.add_argument("--secondary", action="store_true",
-                    help="also time the million-token workload (c5)")
+    ap.add_argument("--no-secondary", dest="secondary", action="store_false",
+                    help="do not also time the million-token workload (c5), which the default "
+                         "run times beside the headline workload")
     ap.add_argument("--cold", action="store_true",
                     help="overwrite 1 GiB between steps (outside the events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -265,6 +265,48 @@ def bsl_version():
 
 # ------------------------------------------------------ torch convenience
 
+def require(name, t, dtype, shape, device):
+    """Raise ValueError unless ``t`` is a contiguous CUDA tensor of this dtype
+    and shape on ``device`` (the device of q: every pointer a call takes must
+    be memory that GPU can read or write; a host tensor's address handed to a
+    kernel would fault it)."""
+    if t.device != device:
+        raise ValueError(f"{name} must be a tensor on {device} (the device of q)")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+
+
+def check_padded(q, k, v, o, seqlens, lse, dtype):
+    """Tensors of a padded-layout call: q, k, v, o [batch, heads, n, d] of the
+    plan's dtype, seqlens int32 [batch] (or None), lse float32 [batch, heads, n]
+    (or None), all contiguous on q's device."""
+    import torch
+    if not getattr(q, "is_cuda", False):
+        raise ValueError("q must be a CUDA tensor")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        require(name, t, dtype, tuple(q.shape), q.device)
+    if seqlens is not None:
+        require("seqlens", seqlens, torch.int32, (q.shape[0],), q.device)
+    if lse is not None:
+        require("lse", lse, torch.float32, tuple(q.shape[:3]), q.device)
+
+
+def check_packed(q, k, v, o, cu_seqlens, lse, dtype):
+    """Tensors of a packed-layout call: q, k, v, o [tokens, heads, d] of the
+    plan's dtype, cu_seqlens int32 [batch + 1], lse float32 [heads, tokens]
+    (or None), all contiguous on q's device."""
+    import torch
+    if not getattr(q, "is_cuda", False):
+        raise ValueError("q must be a CUDA tensor")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        require(name, t, dtype, tuple(q.shape), q.device)
+    if cu_seqlens is None or cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1:
+        raise ValueError("cu_seqlens must be an int32 CUDA tensor of shape [batch + 1]")
+    require("cu_seqlens", cu_seqlens, torch.int32, tuple(cu_seqlens.shape), q.device)
+    if lse is not None:
+        require("lse", lse, torch.float32, (q.shape[1], q.shape[0]), q.device)
+
+
 class Plan:
     """A plan plus shape/dtype checks for torch tensors on the current GPU."""
 
@@ -291,21 +333,14 @@ class Plan:
         except Exception:
             pass
 
-    def _check_tensors(self, q, k, v, o, seqlens, lse):
+    def _tdt(self):
         import torch
-        tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[self.dtype]
+        return {"bf16": torch.bfloat16, "f32": torch.float32}[self.dtype]
+
+    def _check_tensors(self, q, k, v, o, seqlens, lse):
         if q.dim() != 4 or q.shape[1] != self.heads or q.shape[3] != self.head_dim:
             raise ValueError(f"q must be [batch, {self.heads}, n, {self.head_dim}]")
-        for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
-            if t.shape != q.shape or t.dtype != tdt or not t.is_cuda or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous {tdt} CUDA tensor of shape "
-                                 f"{tuple(q.shape)}")
-        if seqlens is not None and (seqlens.dtype != torch.int32 or not seqlens.is_cuda
-                                    or seqlens.shape != (q.shape[0],)):
-            raise ValueError("seqlens must be an int32 CUDA tensor of shape [batch]")
-        if lse is not None and (lse.dtype != torch.float32 or lse.shape != q.shape[:3]
-                                or not lse.is_contiguous()):
-            raise ValueError("lse must be a contiguous float32 tensor of shape [batch, heads, n]")
+        check_padded(q, k, v, o, seqlens, lse, self._tdt())
 
     def forward(self, q, k, v, seqlens=None, o=None, lse=None, stream=None):
         import torch
@@ -333,21 +368,11 @@ class Plan:
         [batch + 1] on the device; lse float32 [heads, tokens].  See
         bsl_forward_varlen in include/bsl.h."""
         import torch
-        tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[self.dtype]
         if o is None:
             o = torch.empty_like(q)
         if q.dim() != 3 or q.shape[1] != self.heads or q.shape[2] != self.head_dim:
             raise ValueError(f"q must be [tokens, {self.heads}, {self.head_dim}]")
-        for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
-            if t.shape != q.shape or t.dtype != tdt or not t.is_cuda or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous {tdt} CUDA tensor of shape "
-                                 f"{tuple(q.shape)}")
-        if (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1
-                or cu_seqlens.shape[0] < 1):
-            raise ValueError("cu_seqlens must be an int32 CUDA tensor of shape [batch + 1]")
-        if lse is not None and (lse.dtype != torch.float32 or lse.shape != (self.heads, q.shape[0])
-                                or not lse.is_contiguous()):
-            raise ValueError("lse must be a contiguous float32 tensor of shape [heads, tokens]")
+        check_packed(q, k, v, o, cu_seqlens, lse, self._tdt())
         bsl_forward_varlen(self.handle, cu_seqlens.shape[0] - 1, q.shape[0], max_seqlen, q, k, v,
                            o, cu_seqlens, lse, stream)
         return o
@@ -366,17 +391,12 @@ class Plan:
             delta = torch.empty((self.heads, q.shape[0]), dtype=torch.float32, device=q.device)
         if q.dim() != 3 or q.shape[1] != self.heads or q.shape[2] != self.head_dim:
             raise ValueError(f"q must be [tokens, {self.heads}, {self.head_dim}]")
-        for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk),
-                        ("dv", dv)):
-            if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous tensor like q")
-        for name, t in (("lse", lse), ("delta", delta)):
-            if (t.dtype != torch.float32 or t.shape != (self.heads, q.shape[0])
-                    or not t.is_contiguous()):
-                raise ValueError(f"{name} must be a contiguous float32 tensor of shape "
-                                 "[heads, tokens]")
-        if (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1):
-            raise ValueError("cu_seqlens must be an int32 CUDA tensor of shape [batch + 1]")
+        if lse is None:
+            raise ValueError("the backward pass needs the lse the forward wrote")
+        check_packed(q, k, v, o, cu_seqlens, lse, self._tdt())
+        for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+            require(name, t, q.dtype, tuple(q.shape), q.device)
+        require("delta", delta, torch.float32, (self.heads, q.shape[0]), q.device)
         bsl_backward_varlen(self.handle, cu_seqlens.shape[0] - 1, q.shape[0], max_seqlen, q, k, v,
                             o, dout, lse, cu_seqlens, dq, dk, dv, delta, stream)
         return dq, dk, dv
@@ -392,15 +412,12 @@ class Plan:
         dv = torch.empty_like(q) if dv is None else dv
         if delta is None:
             delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-        self._check_tensors(q, k, v, o, seqlens, lse)
-        for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
-            if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous tensor like q")
         if lse is None:
             raise ValueError("the backward pass needs the lse the forward wrote")
-        if (delta.dtype != torch.float32 or delta.shape != q.shape[:3]
-                or not delta.is_contiguous()):
-            raise ValueError("delta must be a contiguous float32 tensor of shape [batch, heads, n]")
+        self._check_tensors(q, k, v, o, seqlens, lse)
+        for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+            require(name, t, q.dtype, tuple(q.shape), q.device)
+        require("delta", delta, torch.float32, tuple(q.shape[:3]), q.device)
         bsl_backward(self.handle, q.shape[0], q.shape[2], q, k, v, o, dout, lse, seqlens, dq, dk,
                      dv, delta, stream)
         return dq, dk, dv

@@ -39,6 +39,39 @@ bsl_status fail(bsl_status s, const char *fmt, ...)
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+bool overlaps(const void *a, size_t an, const void *b, size_t bn)
+{
+    const uint8_t *x = (const uint8_t *)a, *y = (const uint8_t *)b;
+    return x < y + bn && y < x + an;
+}
+
+// A buffer the forward writes (o, lse, trace) or reads besides q, k, v (the
+// lengths or offsets), with its size in bytes; ptr may be NULL (absent).
+struct Span {
+    const void *ptr;
+    size_t bytes;
+    const char *name;
+};
+
+// Every pair of spans in `w` (written) must be disjoint, and each must be
+// disjoint from every span in `r` (read).  Absent (NULL) spans are skipped.
+template <size_t NW, size_t NR>
+bsl_status check_disjoint(const Span (&w)[NW], const Span (&r)[NR])
+{
+    for (size_t a = 0; a < NW; ++a) {
+        if (!w[a].ptr)
+            continue;
+        for (size_t b = 0; b < NR; ++b)
+            if (r[b].ptr && overlaps(w[a].ptr, w[a].bytes, r[b].ptr, r[b].bytes))
+                return fail(BSL_E_INVALID, "%s overlaps %s", w[a].name, r[b].name);
+        for (size_t b = a + 1; b < NW; ++b)
+            if (w[b].ptr && overlaps(w[a].ptr, w[a].bytes, w[b].ptr, w[b].bytes))
+                return fail(BSL_E_INVALID, "%s overlaps %s", w[a].name, w[b].name);
+    }
+    return BSL_OK;
+}
 
 // The block band the kernels sweep: R itself, or with a token window W the
 // ceil(W / 32) blocks on either side that hold every key within W tokens.
@@ -75,14 +108,27 @@ bsl_status run(const bsl_plan *plan, int32_t batch, int32_t n, const void *q, co
     const long long nblk = n / d.block_size;
     if ((long long)batch * d.heads * nblk > 0x7fffffffLL)
         return fail(BSL_E_INVALID, "batch * heads * n / 32 exceeds 2^31 - 1");
-    const uint8_t *ob = (const uint8_t *)o;
+    if (lse && !aligned16(lse))
+        return fail(BSL_E_INVALID, "lse must be 16-byte aligned");
+    if (traced && (!aligned4(active) || !aligned4(masks)))
+        return fail(BSL_E_INVALID, "active and masks must be 4-byte aligned");
+    const int32_t radius = band_radius(d);
+    // trace slots: batch * nblk * (2R + 1) words, 32 more per slot for the masks
+    const long double slots = (long double)batch * (long double)nblk * (2.0L * radius + 1.0L);
+    if (traced && slots * 128.0L > 9.0e18L)
+        return fail(BSL_E_INVALID, "the trace of %d x %lld blocks x %d slots is too large", batch,
+                    nblk, 2 * radius + 1);
     const size_t esz = d.dtype == BSL_BF16 ? 2 : 4;
     const size_t bytes = (size_t)elems * esz;
-    for (const void *in : {q, k, v}) {
-        const uint8_t *ib = (const uint8_t *)in;
-        if (ib < ob + bytes && ob < ib + bytes)
-            return fail(BSL_E_INVALID, "o overlaps one of q, k, v");
-    }
+    const size_t rows = (size_t)batch * (size_t)d.heads * (size_t)n;
+    const Span written[] = {{o, bytes, "o"},
+                            {lse, rows * 4, "lse"},
+                            {traced ? active : nullptr, (size_t)slots * 4, "active"},
+                            {traced ? masks : nullptr, (size_t)slots * 128, "masks"}};
+    const Span read[] = {{q, bytes, "q"}, {k, bytes, "k"}, {v, bytes, "v"},
+                         {seqlens, (size_t)batch * 4, "seqlens"}};
+    if (const bsl_status st = check_disjoint(written, read))
+        return st;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess)
         return fail(BSL_E_DEVICE, "hipGetDevice failed");
@@ -105,7 +151,7 @@ bsl_status run(const bsl_plan *plan, int32_t batch, int32_t n, const void *q, co
     a.n = n;
     a.tokens = 0;
     a.head_dim = d.head_dim;
-    a.radius = band_radius(d);
+    a.radius = radius;
     a.window = d.window;
     a.causal = d.causal != 0;
     a.scale = plan->scale;
@@ -114,12 +160,6 @@ bsl_status run(const bsl_plan *plan, int32_t batch, int32_t n, const void *q, co
     if (e != hipSuccess)
         return fail(BSL_E_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return BSL_OK;
-}
-
-bool overlaps(const void *a, size_t an, const void *b, size_t bn)
-{
-    const uint8_t *x = (const uint8_t *)a, *y = (const uint8_t *)b;
-    return x < y + bn && y < x + an;
 }
 
 bsl_status run_varlen(const bsl_plan *plan, int32_t batch, int32_t tokens, int32_t max_seqlen,
@@ -147,11 +187,15 @@ bsl_status run_varlen(const bsl_plan *plan, int32_t batch, int32_t tokens, int32
     const long long nblk = ((long long)max_seqlen + d.block_size - 1) / d.block_size;
     if ((long long)batch * d.heads * nblk > 0x7fffffffLL)
         return fail(BSL_E_INVALID, "batch * heads * ceil(max_seqlen / 32) exceeds 2^31 - 1");
+    if (lse && !aligned16(lse))
+        return fail(BSL_E_INVALID, "lse must be 16-byte aligned");
     const size_t esz = d.dtype == BSL_BF16 ? 2 : 4;
     const size_t bytes = (size_t)elems * esz;
-    for (const void *in : {q, k, v})
-        if (overlaps(o, bytes, in, bytes))
-            return fail(BSL_E_INVALID, "o overlaps one of q, k, v");
+    const Span written[] = {{o, bytes, "o"}, {lse, (size_t)d.heads * (size_t)tokens * 4, "lse"}};
+    const Span read[] = {{q, bytes, "q"}, {k, bytes, "k"}, {v, bytes, "v"},
+                         {cu_seqlens, ((size_t)batch + 1) * 4, "cu_seqlens"}};
+    if (const bsl_status st = check_disjoint(written, read))
+        return st;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess)
         return fail(BSL_E_DEVICE, "hipGetDevice failed");
@@ -255,6 +299,13 @@ bsl_status run_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
     const size_t rb = (size_t)batch * d.heads * (size_t)n * 4;     // one float row vector
     if (const bsl_status st = check_bwd_buffers(plan, ins, outs, tb, rb, true))
         return st;
+    {
+        const Span written[] = {{dq, tb, "dq"}, {dk, tb, "dk"}, {dv, tb, "dv"},
+                                {delta, rb, "delta"}};
+        const Span read[] = {{seqlens, (size_t)batch * 4, "seqlens"}};
+        if (const bsl_status st = check_disjoint(written, read))
+            return st;
+    }
 
     bsl::BwdLaunch a;
     a.q = q;
@@ -321,6 +372,13 @@ bsl_status run_backward_varlen(const bsl_plan *plan, int32_t batch, int32_t toke
     const size_t rb = (size_t)d.heads * (size_t)tokens * 4;       // one float row vector
     if (const bsl_status st = check_bwd_buffers(plan, ins, outs, tb, rb, true))
         return st;
+    {
+        const Span written[] = {{dq, tb, "dq"}, {dk, tb, "dk"}, {dv, tb, "dv"},
+                                {delta, rb, "delta"}};
+        const Span read[] = {{cu_seqlens, ((size_t)batch + 1) * 4, "cu_seqlens"}};
+        if (const bsl_status st = check_disjoint(written, read))
+            return st;
+    }
 
     bsl::BwdLaunch a;
     a.q = q;

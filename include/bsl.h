@@ -100,9 +100,12 @@ bsl_status bsl_create(const bsl_desc *desc, bsl_plan **plan);
  *   lse     device float[batch][heads][n] or NULL: natural-log log-sum-exp of
  *           each row's scaled scores over its kept keys; -inf on padded rows.
  *   stream  a hipStream_t, or NULL for the default stream.
+ * q, k, v, o and lse are 16-byte aligned.  The buffers the call writes (o, lse)
+ * overlap neither each other nor any buffer it reads (q, k, v, seqlens).
  * Returns BSL_E_INVALID for a NULL plan, negative sizes, n % 32 != 0, a NULL
- * q/k/v/o when batch * n > 0, or sizes whose element count does not fit in 63
- * bits; BSL_E_INVALID also when the current device is not the plan's. */
+ * q/k/v/o when batch * n > 0, a misaligned pointer, overlapping buffers, or
+ * sizes whose element count does not fit in 63 bits; BSL_E_INVALID also when
+ * the current device is not the plan's. */
 bsl_status bsl_forward(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
                        const void *k, const void *v, void *o, const int32_t *seqlens,
                        float *lse, void *stream);
@@ -115,8 +118,9 @@ bsl_status bsl_forward(const bsl_plan *plan, int32_t batch, int32_t n, const voi
  *   masks   device uint32[batch][n/32][2R+1][32]: for slot s of query block i,
  *           word r has bit c set iff the kernel kept key c of that key block
  *           for query row r; zero for unused slots and padded query rows.
- * Both are required (non-NULL) and are written in full; they describe head 0
- * (the band and the masks are the same for every head). */
+ * Both are required (non-NULL), 4-byte aligned, and are written in full; they
+ * describe head 0 (the band and the masks are the same for every head).  Like
+ * o and lse they overlap no other buffer of the call (BSL_E_INVALID). */
 bsl_status bsl_forward_traced(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
                               const void *k, const void *v, void *o, const int32_t *seqlens,
                               float *lse, int32_t *active, uint32_t *masks, void *stream);
@@ -153,7 +157,8 @@ bsl_status bsl_forward_traced(const bsl_plan *plan, int32_t batch, int32_t n, co
  *   stream      a hipStream_t, or NULL for the default stream.
  * batch, tokens or max_seqlen == 0 is a no-op returning BSL_OK.  Returns
  * BSL_E_INVALID for a NULL plan or cu_seqlens, negative sizes, a NULL or
- * misaligned (not 16-byte) q/k/v/o, o overlapping an input, sizes past the
+ * misaligned (not 16-byte) q/k/v/o, a misaligned lse, o or lse overlapping
+ * each other or a buffer the call reads (q, k, v, cu_seqlens), sizes past the
  * limits of bsl_forward, or a current device that is not the plan's. */
 bsl_status bsl_forward_varlen(const bsl_plan *plan, int32_t batch, int32_t tokens,
                               int32_t max_seqlen, const void *q, const void *k, const void *v,
@@ -189,7 +194,7 @@ bsl_status bsl_varlen_offsets(int32_t batch, const int32_t *lengths, int32_t *cu
  *            call overwrites it with D (0 on padded rows).  The library
  *            allocates nothing.
  * All tensors 16-byte aligned.  dq, dk, dv and delta must not overlap each
- * other or any input.  A plan with a token window differentiates the window
+ * other or any input (seqlens included).  A plan with a token window differentiates the window
  * forward.  Returns BSL_E_INVALID for the argument errors bsl_forward
  * rejects, a NULL pointer, misalignment or overlap, and BSL_E_DEVICE if a
  * launch fails.

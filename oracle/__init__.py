@@ -84,8 +84,12 @@ def load(path=None):
     if path is not None:
         return _declare(ctypes.CDLL(path))
     if _lib is None:
-        lib_path = os.path.join(_HERE, "liborc.so")
+        # ORC_LIBRARY selects another build of the same source (the sanitizer
+        # build of tests/test_host_sanitize.py); unset, the in-tree build
+        lib_path = os.environ.get("ORC_LIBRARY") or os.path.join(_HERE, "liborc.so")
         if not os.path.exists(lib_path):
+            if os.environ.get("ORC_LIBRARY"):
+                raise OracleError(f"ORC_LIBRARY={lib_path} does not exist")
             _build.build()
         _lib = _declare(ctypes.CDLL(lib_path))
     return _lib
