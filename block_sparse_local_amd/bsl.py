@@ -24,7 +24,8 @@ BSL_BF16, BSL_F32 = 0, 1
 
 # every function include/bsl.h declares
 EXPORTS = ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_forward_varlen",
-           "bsl_varlen_offsets", "bsl_backward", "bsl_backward_varlen", "bsl_kmer_tokenize",
+           "bsl_varlen_offsets", "bsl_backward", "bsl_backward_noalloc", "bsl_backward_varlen",
+           "bsl_kmer_tokenize",
            "bsl_kmer_ceiling", "bsl_check_seqlens", "bsl_check_cu_seqlens", "bsl_destroy", "bsl_status_string",
            "bsl_last_error", "bsl_version")
 
@@ -73,6 +74,8 @@ def load(path=LIB_PATH):
     i32p = ctypes.POINTER(i32)
     lib.bsl_varlen_offsets.argtypes = [i32, i32p, i32p, i32p, i32p]
     lib.bsl_backward.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.bsl_backward_noalloc.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         vp]
     lib.bsl_backward_varlen.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                         vp, vp]
     lib.bsl_kmer_tokenize.argtypes = [i32, vp, ctypes.c_int64, vp, i32, i32, vp, vp, vp]
@@ -87,8 +90,9 @@ def load(path=LIB_PATH):
     lib.bsl_version.argtypes = []
     lib.bsl_version.restype = i32
     for name in ("bsl_create", "bsl_forward", "bsl_forward_traced", "bsl_forward_varlen",
-                 "bsl_varlen_offsets", "bsl_backward", "bsl_backward_varlen", "bsl_kmer_tokenize",
-                 "bsl_kmer_ceiling", "bsl_check_seqlens", "bsl_check_cu_seqlens", "bsl_destroy"):
+                 "bsl_varlen_offsets", "bsl_backward", "bsl_backward_noalloc",
+                 "bsl_backward_varlen", "bsl_kmer_tokenize", "bsl_kmer_ceiling",
+                 "bsl_check_seqlens", "bsl_check_cu_seqlens", "bsl_destroy"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -162,6 +166,13 @@ def bsl_backward(plan, batch, n, q, k, v, o, dout, lse, seqlens, dq, dk, dv, del
     _check(load().bsl_backward(plan, batch, n, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
                                _ptr(lse), _ptr(seqlens), _ptr(dq), _ptr(dk), _ptr(dv),
                                _ptr(delta), _stream(stream)))
+
+
+def bsl_backward_noalloc(plan, batch, n, q, k, v, o, dout, lse, seqlens, dq, dk, dv,
+                         stream=None):
+    _check(load().bsl_backward_noalloc(plan, batch, n, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                       _ptr(dout), _ptr(lse), _ptr(seqlens), _ptr(dq), _ptr(dk),
+                                       _ptr(dv), _stream(stream)))
 
 
 def bsl_backward_varlen(plan, batch, tokens, max_seqlen, q, k, v, o, dout, lse, cu_seqlens, dq,

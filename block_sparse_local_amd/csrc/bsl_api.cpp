@@ -7,6 +7,7 @@
 #include "check.h"
 #include "kmer_launch.h"
 #include "launch.h"
+#include "scratch.h"
 
 #include <hip/hip_runtime.h>
 
@@ -472,6 +473,12 @@ bsl_status bsl_create(const bsl_desc *desc, bsl_plan **plan)
         return fail(BSL_E_UNSUPPORTED, "device %d is %s; this library is built for gfx950", dev,
                     prop.gcnArchName);
 
+    // the fixed workspace of bsl_backward_noalloc: its address on this device,
+    // looked up once per device while the device is current
+    if (const hipError_t e = bsl::scratch_setup(dev); e != hipSuccess)
+        return fail(BSL_E_DEVICE, "the fixed device workspace of device %d was not found: %s",
+                    dev, hipGetErrorString(e));
+
     bsl_plan *p = new (std::nothrow) bsl_plan;
     if (!p)
         return fail(BSL_E_NOMEM, "out of host memory");
@@ -503,6 +510,28 @@ bsl_status bsl_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
                         float *delta, void *stream)
 {
     return run_backward(plan, batch, n, q, k, v, o, dout, lse, seqlens, dq, dk, dv, delta, stream);
+}
+
+bsl_status bsl_backward_noalloc(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
+                                const void *k, const void *v, const void *o, const void *dout,
+                                const float *lse, const int32_t *seqlens, void *dq, void *dk,
+                                void *dv, void *stream)
+{
+    if (!plan)
+        return fail(BSL_E_INVALID, "plan is NULL");
+    if (batch > 0 && n > 0) {
+        const long long rows = (long long)batch * plan->desc.heads * (long long)n;
+        if (rows > (long long)bsl::SCRATCH_FLOATS)
+            return fail(BSL_E_UNSUPPORTED,
+                        "batch * heads * n = %lld rows; the fixed workspace of "
+                        "bsl_backward_noalloc holds %zu rows (%zu MiB): use bsl_backward",
+                        rows, bsl::SCRATCH_FLOATS, bsl::SCRATCH_FLOATS * 4 >> 20);
+    }
+    float *const ws = bsl::scratch_on(plan->device);
+    if (!ws)
+        return fail(BSL_E_DEVICE, "the fixed device workspace of device %d was not found",
+                    plan->device);
+    return run_backward(plan, batch, n, q, k, v, o, dout, lse, seqlens, dq, dk, dv, ws, stream);
 }
 
 bsl_status bsl_backward_varlen(const bsl_plan *plan, int32_t batch, int32_t tokens,

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define BSL_VERSION 10600 /* major * 10000 + minor * 100 + patch */
+#define BSL_VERSION 10700 /* major * 10000 + minor * 100 + patch */
 
 typedef enum bsl_status {
     BSL_OK = 0,
@@ -203,6 +203,25 @@ bsl_status bsl_backward(const bsl_plan *plan, int32_t batch, int32_t n, const vo
                         const void *k, const void *v, const void *o, const void *dout,
                         const float *lse, const int32_t *seqlens, void *dq, void *dk, void *dv,
                         float *delta, void *stream);
+
+/* bsl_backward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same gradients from the same kernels, bit for bit, with the row vector D
+ * kept in a fixed workspace of the library instead of a caller's delta.
+ *   Arguments as bsl_backward, without delta.
+ * The workspace is one file-scope device array of 8 Mi floats (32 MiB) that
+ * every device the library runs on holds until the process ends; this call
+ * allocates nothing.  batch * heads * n may be at most 8,388,608 (8 Mi) rows:
+ * beyond that the call returns BSL_E_UNSUPPORTED (use bsl_backward).  Every
+ * call on one device uses that device's one workspace, so calls that overlap
+ * in time on the same device (other streams, other threads) race and must not
+ * be made; calls in order on one stream are safe.  Nothing in the workspace
+ * needs to start at zero: each call writes every row it reads.  Other errors
+ * as bsl_backward. */
+bsl_status bsl_backward_noalloc(const bsl_plan *plan, int32_t batch, int32_t n, const void *q,
+                                const void *k, const void *v, const void *o, const void *dout,
+                                const float *lse, const int32_t *seqlens, void *dq, void *dk,
+                                void *dv, void *stream);
 
 /* bsl_backward over the packed layout of bsl_forward_varlen: the same
  * gradients per sequence, each sequence alone, with the rows back to back.

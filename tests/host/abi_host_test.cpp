@@ -238,6 +238,31 @@ void test_backward()
     EXPECT(fake::state().bwd_valu == 1 && fake::state().last_bwd_valu_bf16);
     bsl_destroy(p);
 
+    // no-alloc variant: the library's fixed workspace stands in for delta
+    const int lookups = fake::state().scratch_lookups;
+    bsl_plan *p2 = make_plan(64, heads, 1, 0, BSL_BF16);
+    EXPECT(fake::state().scratch_lookups == lookups); // once per device, not per plan
+    const int nb0 = fake::state().bwd_bf16;
+    EXPECT(bsl_backward_noalloc(p2, batch, n, q, k, v, o, g, lse, sl, dq, dk, dv, nullptr) ==
+           BSL_OK);
+    EXPECT(fake::state().bwd_bf16 == nb0 + 1 &&
+           fake::state().last_bwd.delta == fake::state().scratch);
+    EXPECT_REJECTED(bsl_backward_noalloc(p2, batch, n, q, k, v, o, g, lse, sl, dq, dq, dv,
+                                         nullptr));
+    EXPECT_REJECTED(bsl_backward_noalloc(nullptr, batch, n, q, k, v, o, g, lse, sl, dq, dk, dv,
+                                         nullptr));
+    {
+        // 8 Mi rows is the limit: 2 x 2 x 2^21 rows fits, one more block does not
+        const int before = fake::state().launches();
+        EXPECT(bsl_backward_noalloc(p2, 2, 2 << 20, q, k, v, o, g, lse, nullptr, dq, dk, dv,
+                                    nullptr) != BSL_E_UNSUPPORTED);
+        EXPECT(bsl_backward_noalloc(p2, 2, (2 << 20) + 32, q, k, v, o, g, lse, nullptr, dq, dk,
+                                    dv, nullptr) == BSL_E_UNSUPPORTED);
+        EXPECT(std::strstr(bsl_last_error(), "fixed workspace") != nullptr);
+        EXPECT(fake::state().launches() <= before + 1);
+    }
+    bsl_destroy(p2);
+
     // packed layout
     const int tokens = 90;
     p = make_plan(128, 1, 1, 1, BSL_BF16);
@@ -286,7 +311,10 @@ void test_host_helpers()
 
 int main()
 {
+    static float workspace[64];
+    fake::state().scratch = workspace;
     test_create();
+    EXPECT(fake::state().scratch_lookups == 1); // looked up by the first bsl_create
     test_forward();
     test_forward_varlen();
     test_backward();

@@ -76,6 +76,23 @@ hipError_t launch_kmer(const KmerLaunch &a)
     return fake::state().launch_result;
 }
 
+namespace {
+float *g_scratch[8] = {};
+}
+
+hipError_t scratch_setup(int device)
+{
+    if (device < 0 || device > 7)
+        return hipErrorInvalidDevice;
+    if (!g_scratch[device]) {
+        fake::state().scratch_lookups++;
+        g_scratch[device] = fake::state().scratch;
+    }
+    return hipSuccess;
+}
+
+float *scratch_on(int device) { return device < 0 || device > 7 ? nullptr : g_scratch[device]; }
+
 hipError_t launch_check(const int32_t *, int32_t, int32_t, int, int32_t *, hipStream_t)
 {
     fake::state().check++;

@@ -11,6 +11,7 @@
 #include "check.h"
 #include "kmer_launch.h"
 #include "launch.h"
+#include "scratch.h"
 
 namespace fake {
 
@@ -19,6 +20,8 @@ struct State {
     const char *arch = "gfx950:sramecc+:xnack-"; // gcnArchName of every device
     hipError_t launch_result = hipSuccess;       // what every launcher returns
     int fwd_bf16 = 0, fwd_f32 = 0, bwd_bf16 = 0, bwd_valu = 0, kmer = 0, check = 0;
+    int scratch_lookups = 0;           // scratch_setup calls that did a lookup
+    float *scratch = nullptr;          // the workspace "address" of every device
     bool last_bwd_valu_bf16 = false;
     bsl::Launch last_fwd{};
     bsl::BwdLaunch last_bwd{};
