@@ -47,6 +47,8 @@ VARIANTS = {
     "eager-rescale": (["-DBSL_RESCALE_SLACK=0.0f"], True),
     "eager-exchange": (["-DBSL_LAZY_EXCHANGE=0"], True),
     "agpr-accumulators": ([], False),
+    "global-ring-loads": (["-DBSL_RING_BUFFER_LOADS=0"], True),
+    "narrow-stores": (["-DBSL_WIDE_STORES=0"], True),
 }
 
 

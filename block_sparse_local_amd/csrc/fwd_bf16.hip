@@ -66,6 +66,11 @@ namespace {
 //   BSL_RESCALE_SLACK move the reference maximum only when a row's maximum
 //                     exceeds it by more than this (log2 units; 0: on any rise)
 //   BSL_LAZY_EXCHANGE 1: exchange half-column maxima only on a move; 0: always
+//   BSL_RING_BUFFER_LOADS 1: ring loads are buffer loads into LDS (a scalar
+//                     resource per block, loop-invariant lane offsets);
+//                     0: global loads into LDS with a 64-bit address per lane
+//   BSL_WIDE_STORES   1: O rows reassembled across the lane pair and stored
+//                     16 bytes at a time; 0: each lane stores its 8-byte halves
 #ifndef BSL_SWIZZLE
 #define BSL_SWIZZLE 1
 #endif
@@ -80,6 +85,12 @@ namespace {
 #endif
 #ifndef BSL_LAZY_EXCHANGE
 #define BSL_LAZY_EXCHANGE 1
+#endif
+#ifndef BSL_RING_BUFFER_LOADS
+#define BSL_RING_BUFFER_LOADS 1
+#endif
+#ifndef BSL_WIDE_STORES
+#define BSL_WIDE_STORES 1
 #endif
 
 constexpr float RESCALE_SLACK = BSL_RESCALE_SLACK; // in log2 units
@@ -299,7 +310,13 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
                     off -= (uint32_t)(r - last) * (uint32_t)(RS * 2);
             }
             uint8_t *dst = lds + stage * STAGE + (u * NT + wave * 64) * 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_v ? vrs : krs, (lds_void *)dst, 16, off, 0, 0, 0);
+            if (BSL_RING_BUFFER_LOADS)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(is_v ? vrs : krs, (lds_void *)dst, 16, off, 0,
+                                                         0, 0);
+            else
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)((const uint8_t *)(is_v ? vg : kg) + (size_t)j * BLK * RS * 2 + off),
+                    (lds_void *)dst, 16, 0, 0);
         }
     };
 
@@ -492,6 +509,12 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
             }
             pk4[a] = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(lo2, bf16x2)),
                            __builtin_bit_cast(uint32_t, __builtin_convertvector(hi2, bf16x2))};
+        }
+        if (!BSL_WIDE_STORES) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                *(u32x2 *)(orow + m * 32 + 8 * a + 4 * half) = pk4[a];
+            continue;
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
