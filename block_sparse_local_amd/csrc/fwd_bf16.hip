@@ -321,22 +321,34 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
     };
 
     // ----------------------------------------------------------- Q fragment
+    // Every lane loads, so that no load sits in a branch: a lane without a
+    // query of its own reads the sequence's first row (it exists: len >= 1
+    // here), and zeroes it by select below, once the loads have landed.
     const int qrow = i * BLK + col;
     const bool qvalid = exists && qrow < len;
+    const int qread = qvalid ? qrow : 0;
     bf16x8 qf[NKS];
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-        u32x4 x = u32x4{0, 0, 0, 0};
-        if (qvalid)
-            x = *(const u32x4 *)(qg + (size_t)qrow * RS + s * 16 + half * 8);
-        qf[s] = as_bf16x8(x);
-    }
+    for (int s = 0; s < NKS; ++s)
+        qf[s] = as_bf16x8(*(const u32x4 *)(qg + (size_t)qread * RS + s * 16 + half * 8));
 
-    // start the ring before waiting on anything
+    // Start the ring before waiting on anything.  Every stage but the last is
+    // filled, a sweep shorter than that repeating its last block into a stage
+    // it never reads, so that the count of loads in flight is the same on
+    // every path.
 #pragma unroll
     for (int a = 0; a < NSTAGE - 1; ++a)
-        if (a < L)
-            issue(block_at(a), a);
+        issue(block_at(a < L ? a : L - 1), a);
+    // Wait for the Q fragment here, with the ring's loads still in flight.  The
+    // empty asm takes Q over as its own result, so the loop below uses no
+    // register loaded outside it; otherwise the compiler drains every load in
+    // flight, the whole ring included, before entering the loop.
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+        if (!qvalid)
+            qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+        __asm__ volatile("" : "+v"(qf[s]));
+    }
 
     f32x16 oacc[NMT];
 #pragma unroll
