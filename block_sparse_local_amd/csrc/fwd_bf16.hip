@@ -300,9 +300,10 @@ __global__ void __launch_bounds__(MQ * 64) fwd_bf16_kernel(Params p)
                 continue; // whole waves only: SLOTS is a multiple of 64
             const bool is_v = u * NT + wave * 64 >= SLOTS / 2; // uniform per wave
             uint32_t off = loff[u];
-            if (VARLEN) {
-                // packed layout: rows past the end repeat the last row (in
-                // bounds; masked below); the padded buffer holds all 32 rows
+            if (VARLEN && (j + 1) * BLK > len) {
+                // packed layout, the sequence's last block: rows past the end
+                // repeat the last row (in bounds; masked below); the padded
+                // buffer holds all 32 rows of every block
                 const int t = (is_v ? u * NT + tid - SLOTS / 2 : u * NT + tid);
                 const int r = t / T::CPR;
                 const int last = len - 1 - j * BLK;
