@@ -195,6 +195,62 @@ __device__ __forceinline__ void tr_frags(const uint8_t *tile, int m, int tr_row,
     a1 = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// The transposed operands of every output tile (NMT of them) in one go: all
+// 4 NMT transposing reads issued back to back and waited for once, so a wave
+// that has the SIMD to itself pays the LDS latency once per product instead of
+// once per tile.
+template <int D>
+__device__ __forceinline__ void tr_frags_all(const uint8_t *tile, int tr_row, int tr_col, bf16x8 (&a0)[D / 32],
+                                             bf16x8 (&a1)[D / 32])
+{
+    using T = BTile<D>;
+    constexpr int NMT = D / 32;
+    const uint32_t base = (uint32_t)(size_t)(lds_u8 *)tile + (tr_col & 7) * 2;
+    uint32_t r0a[NMT], r8a[NMT];
+#pragma unroll
+    for (int m = 0; m < NMT; ++m) {
+        const int chunk = 4 * m + (tr_col >> 3);
+        r0a[m] = base + tr_row * T::ROW_BYTES + ((chunk ^ T::swz(tr_row)) << 4);
+        r8a[m] = base + (tr_row + 8) * T::ROW_BYTES + ((chunk ^ T::swz(tr_row + 8)) << 4);
+    }
+    u32x2 r[NMT][4];
+    if constexpr (NMT == 4) {
+        __asm__ volatile(
+            "ds_read_b64_tr_b16 %0, %16\n\tds_read_b64_tr_b16 %1, %20\n\t"
+            "ds_read_b64_tr_b16 %2, %16 offset:%24\n\tds_read_b64_tr_b16 %3, %20 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %4, %17\n\tds_read_b64_tr_b16 %5, %21\n\t"
+            "ds_read_b64_tr_b16 %6, %17 offset:%24\n\tds_read_b64_tr_b16 %7, %21 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %8, %18\n\tds_read_b64_tr_b16 %9, %22\n\t"
+            "ds_read_b64_tr_b16 %10, %18 offset:%24\n\tds_read_b64_tr_b16 %11, %22 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %12, %19\n\tds_read_b64_tr_b16 %13, %23\n\t"
+            "ds_read_b64_tr_b16 %14, %19 offset:%24\n\tds_read_b64_tr_b16 %15, %23 offset:%24\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3]), "=&v"(r[1][0]),
+              "=&v"(r[1][1]), "=&v"(r[1][2]), "=&v"(r[1][3]), "=&v"(r[2][0]), "=&v"(r[2][1]),
+              "=&v"(r[2][2]), "=&v"(r[2][3]), "=&v"(r[3][0]), "=&v"(r[3][1]), "=&v"(r[3][2]),
+              "=&v"(r[3][3])
+            : "v"(r0a[0]), "v"(r0a[1]), "v"(r0a[2]), "v"(r0a[3]), "v"(r8a[0]), "v"(r8a[1]), "v"(r8a[2]),
+              "v"(r8a[3]), "i"(16 * T::ROW_BYTES));
+    } else {
+        __asm__ volatile(
+            "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %10\n\t"
+            "ds_read_b64_tr_b16 %2, %8 offset:%12\n\tds_read_b64_tr_b16 %3, %10 offset:%12\n\t"
+            "ds_read_b64_tr_b16 %4, %9\n\tds_read_b64_tr_b16 %5, %11\n\t"
+            "ds_read_b64_tr_b16 %6, %9 offset:%12\n\tds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3]), "=&v"(r[1][0]),
+              "=&v"(r[1][1]), "=&v"(r[1][2]), "=&v"(r[1][3])
+            : "v"(r0a[0]), "v"(r0a[1]), "v"(r8a[0]), "v"(r8a[1]), "i"(16 * T::ROW_BYTES));
+    }
+#pragma unroll
+    for (int m = 0; m < NMT; ++m) {
+        const bf16x4 q0 = __builtin_bit_cast(bf16x4, r[m][0]), q1 = __builtin_bit_cast(bf16x4, r[m][1]);
+        const bf16x4 q2 = __builtin_bit_cast(bf16x4, r[m][2]), q3 = __builtin_bit_cast(bf16x4, r[m][3]);
+        a0[m] = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+        a1[m] = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
+
 // Pack 16 fp32 accumulator values into the two bf16 B fragments of a product
 // that contracts over the accumulator's rows.
 __device__ __forceinline__ void pack_b(const float *x, bf16x8 &b0, bf16x8 &b1)
@@ -620,19 +676,23 @@ __global__ void __launch_bounds__(256) dkv_kernel(BParams p)
         bf16x8 pb0, pb1, db0, db1;
         pack_b(pv, pb0, pb1);
         pack_b(ds, db0, db1);
+        {
+            bf16x8 a0[NMT], a1[NMT];
+            tr_frags_all<D>(gl, tr_row, tr_col, a0, a1);
 #pragma unroll
-        for (int m = 0; m < NMT; ++m) {
-            bf16x8 a0, a1;
-            tr_frags<D>(gl, m, tr_row, tr_col, a0, a1);
-            dva[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, pb0, dva[m], 0, 0, 0);
-            dva[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, pb1, dva[m], 0, 0, 0);
+            for (int m = 0; m < NMT; ++m) {
+                dva[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[m], pb0, dva[m], 0, 0, 0);
+                dva[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[m], pb1, dva[m], 0, 0, 0);
+            }
         }
+        {
+            bf16x8 a0[NMT], a1[NMT];
+            tr_frags_all<D>(ql, tr_row, tr_col, a0, a1);
 #pragma unroll
-        for (int m = 0; m < NMT; ++m) {
-            bf16x8 a0, a1;
-            tr_frags<D>(ql, m, tr_row, tr_col, a0, a1);
-            dka[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, db0, dka[m], 0, 0, 0);
-            dka[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, db1, dka[m], 0, 0, 0);
+            for (int m = 0; m < NMT; ++m) {
+                dka[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[m], db0, dka[m], 0, 0, 0);
+                dka[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[m], db1, dka[m], 0, 0, 0);
+            }
         }
     }
     if (exists) {
