@@ -319,12 +319,22 @@ def cpu_baseline_backward(r, target_flops=6.0e11, log=print):
 
 
 def cpu_model():
-    """The host processor's model name (from /proc/cpuinfo), or the platform's."""
+    """The host processor's model name from /proc/cpuinfo, with its family,
+    model and stepping numbers and the logical CPU count (a virtual machine
+    may report only a generic name), or the platform's description."""
     try:
+        info, count = {}, 0
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                key, _, val = line.partition(":")
+                key = key.strip()
+                if key == "processor":
+                    count += 1
+                elif key in ("model name", "cpu family", "model", "stepping") and key not in info:
+                    info[key] = val.strip()
+        if "model name" in info:
+            ids = ", ".join(f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info)
+            return f"{info['model name']} ({ids}; {count} logical CPUs)" if ids else info["model name"]
     except OSError:
         pass
     import platform
