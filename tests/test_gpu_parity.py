@@ -154,7 +154,7 @@ def _rand_case(seed, dtype, dd, radius, causal, nblk, lens, heads=2):
 SMALL = []
 for _dt in ("bf16", "f32"):
     for _dd in (32, 64, 128):
-        for _r, _c in ((0, False), (1, False), (3, True), (8, False), (2, True)):
+        for _r, _c in ((0, False), (1, False), (2, False), (3, True), (8, False), (2, True)):
             SMALL.append((_dt, _dd, _r, _c))
 
 
