@@ -24,6 +24,9 @@
 //    query bands (ring of Q, dO, lse and D blocks).  Per query block
 //        S = Q K^T,  dP = dO V^T  (each lane owns one key column),
 //        dV^T += dO^T P,  dK^T += Q^T dS.
+//    K stays in registers; the wave's V block waits in LDS, which is what
+//    lets the two fp32 accumulators and everything else fit 256 registers at
+//    d 128 (two waves per SIMD) and 168 at d 64 (three).
 // P and dS are rounded once to bf16 for the MFMAs; every sum is fp32.  K (in
 // dq) and Q, dO (in dkv) are read both row-wise and transposed, so their LDS
 // tiles use one swizzle that keeps both access patterns free of bank
@@ -193,62 +196,6 @@ __device__ __forceinline__ void tr_frags(const uint8_t *tile, int m, int tr_row,
     const bf16x4 q2 = __builtin_bit_cast(bf16x4, r2), q3 = __builtin_bit_cast(bf16x4, r3);
     a0 = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
     a1 = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// The transposed operands of every output tile (NMT of them) in one go: all
-// 4 NMT transposing reads issued back to back and waited for once, so a wave
-// that has the SIMD to itself pays the LDS latency once per product instead of
-// once per tile.
-template <int D>
-__device__ __forceinline__ void tr_frags_all(const uint8_t *tile, int tr_row, int tr_col, bf16x8 (&a0)[D / 32],
-                                             bf16x8 (&a1)[D / 32])
-{
-    using T = BTile<D>;
-    constexpr int NMT = D / 32;
-    const uint32_t base = (uint32_t)(size_t)(lds_u8 *)tile + (tr_col & 7) * 2;
-    uint32_t r0a[NMT], r8a[NMT];
-#pragma unroll
-    for (int m = 0; m < NMT; ++m) {
-        const int chunk = 4 * m + (tr_col >> 3);
-        r0a[m] = base + tr_row * T::ROW_BYTES + ((chunk ^ T::swz(tr_row)) << 4);
-        r8a[m] = base + (tr_row + 8) * T::ROW_BYTES + ((chunk ^ T::swz(tr_row + 8)) << 4);
-    }
-    u32x2 r[NMT][4];
-    if constexpr (NMT == 4) {
-        __asm__ volatile(
-            "ds_read_b64_tr_b16 %0, %16\n\tds_read_b64_tr_b16 %1, %20\n\t"
-            "ds_read_b64_tr_b16 %2, %16 offset:%24\n\tds_read_b64_tr_b16 %3, %20 offset:%24\n\t"
-            "ds_read_b64_tr_b16 %4, %17\n\tds_read_b64_tr_b16 %5, %21\n\t"
-            "ds_read_b64_tr_b16 %6, %17 offset:%24\n\tds_read_b64_tr_b16 %7, %21 offset:%24\n\t"
-            "ds_read_b64_tr_b16 %8, %18\n\tds_read_b64_tr_b16 %9, %22\n\t"
-            "ds_read_b64_tr_b16 %10, %18 offset:%24\n\tds_read_b64_tr_b16 %11, %22 offset:%24\n\t"
-            "ds_read_b64_tr_b16 %12, %19\n\tds_read_b64_tr_b16 %13, %23\n\t"
-            "ds_read_b64_tr_b16 %14, %19 offset:%24\n\tds_read_b64_tr_b16 %15, %23 offset:%24\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3]), "=&v"(r[1][0]),
-              "=&v"(r[1][1]), "=&v"(r[1][2]), "=&v"(r[1][3]), "=&v"(r[2][0]), "=&v"(r[2][1]),
-              "=&v"(r[2][2]), "=&v"(r[2][3]), "=&v"(r[3][0]), "=&v"(r[3][1]), "=&v"(r[3][2]),
-              "=&v"(r[3][3])
-            : "v"(r0a[0]), "v"(r0a[1]), "v"(r0a[2]), "v"(r0a[3]), "v"(r8a[0]), "v"(r8a[1]), "v"(r8a[2]),
-              "v"(r8a[3]), "i"(16 * T::ROW_BYTES));
-    } else {
-        __asm__ volatile(
-            "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %10\n\t"
-            "ds_read_b64_tr_b16 %2, %8 offset:%12\n\tds_read_b64_tr_b16 %3, %10 offset:%12\n\t"
-            "ds_read_b64_tr_b16 %4, %9\n\tds_read_b64_tr_b16 %5, %11\n\t"
-            "ds_read_b64_tr_b16 %6, %9 offset:%12\n\tds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3]), "=&v"(r[1][0]),
-              "=&v"(r[1][1]), "=&v"(r[1][2]), "=&v"(r[1][3])
-            : "v"(r0a[0]), "v"(r0a[1]), "v"(r8a[0]), "v"(r8a[1]), "i"(16 * T::ROW_BYTES));
-    }
-#pragma unroll
-    for (int m = 0; m < NMT; ++m) {
-        const bf16x4 q0 = __builtin_bit_cast(bf16x4, r[m][0]), q1 = __builtin_bit_cast(bf16x4, r[m][1]);
-        const bf16x4 q2 = __builtin_bit_cast(bf16x4, r[m][2]), q3 = __builtin_bit_cast(bf16x4, r[m][3]);
-        a0[m] = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
-        a1[m] = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
 }
 
 // Pack 16 fp32 accumulator values into the two bf16 B fragments of a product
@@ -489,8 +436,12 @@ __global__ void __launch_bounds__(256) dq_kernel(BParams p)
 }
 
 // ------------------------------------------------------------------ dkv
+// Occupancy target: the register budget that gives two waves per SIMD at
+// d 128 and three at d 64 (at d 128 the packed-layout instances spill two or
+// three values, none of them inside the loop).
 template <int D, int NSTAGE, bool CAUSAL, bool VARLEN>
-__global__ void __launch_bounds__(256) dkv_kernel(BParams p)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 3)))
+dkv_kernel(BParams p)
 {
     using T = BTile<D>;
     constexpr int MK = 4, NT = 256;
@@ -500,7 +451,8 @@ __global__ void __launch_bounds__(256) dkv_kernel(BParams p)
     constexpr int LPT = TILES / 16 / NT;
     static_assert(TILES / 16 % NT == 0 && LPT >= 1, "slots split evenly over threads");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
+    // the ring, then one V tile per wave
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE + MK * T::BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -567,8 +519,12 @@ __global__ void __launch_bounds__(256) dkv_kernel(BParams p)
         }
     };
 
-    // this wave's key and value fragments (B operands of S = Q K^T, dP = dO V^T)
-    bf16x8 kf[NKS], vf[NKS];
+    // this wave's key and value fragments (B operands of S = Q K^T, dP = dO V^T);
+    // the value fragments go to the wave's own LDS tile, each lane writing the
+    // chunks it reads back in the loop (so no other lane or wave is involved),
+    // and the empty asm keeps the compiler from carrying them in registers
+    bf16x8 kf[NKS];
+    uint8_t *const vtile = lds + NSTAGE * STAGE + wave * T::BYTES;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
         u32x4 x = u32x4{0, 0, 0, 0}, y = u32x4{0, 0, 0, 0};
@@ -577,8 +533,9 @@ __global__ void __launch_bounds__(256) dkv_kernel(BParams p)
             y = *(const u32x4 *)(p.v + base + (size_t)krow * RS + s * 16 + half * 8);
         }
         kf[s] = as_bf16x8(x);
-        vf[s] = as_bf16x8(y);
+        *(u32x4 *)(vtile + col * T::ROW_BYTES + (((2 * s + half) ^ T::swz(col)) << 4)) = y;
     }
+    __asm__ volatile("" ::: "memory");
 
 #pragma unroll
     for (int a = 0; a < NSTAGE - 1; ++a)
@@ -615,6 +572,13 @@ __global__ void __launch_bounds__(256) dkv_kernel(BParams p)
             issue(block_at(t + NSTAGE - 1), (t + NSTAGE - 1) % NSTAGE);
         uint8_t *ql = lds + stage * STAGE;
         uint8_t *gl = ql + T::BYTES;
+        // The V tile is addressed from the Q tile's lane addresses plus a
+        // uniform offset that the compiler cannot see through, so that it does
+        // not keep a second set of per-lane addresses live across the loop
+        // (at d 128 that pushed other values out to scratch, and each reload
+        // then waited for the ring's loads in flight).
+        int voff = (int)(vtile - ql);
+        __asm__ volatile("" : "+s"(voff));
         const float *lsel = (const float *)(ql + TILES);
         const float *dl = lsel + BLK;
         const bool pad_block = i == nb - 1 && (len & (BLK - 1)) != 0;
@@ -642,25 +606,28 @@ __global__ void __launch_bounds__(256) dkv_kernel(BParams p)
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const bf16x8 ga = row_frag<D>(gl, col, 2 * ks + half);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
-        }
-        // lse and D of this lane's 16 query rows: rows 8a + 4 half + (0..3)
-        f32x4 l4[4], d4[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            l4[a] = *(const f32x4 *)(lsel + 8 * a + 4 * half);
-            d4[a] = *(const f32x4 *)(dl + 8 * a + 4 * half);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, row_frag<D>(ql + voff, col, 2 * ks + half), dp,
+                                                         0, 0, 0);
         }
         const int di = i > j ? i - j : j - i;
         const bool need_mask = !kvalid || pad_block || (CAUSAL && i == j) ||
                                (p.window > 0 && di * BLK + BLK - 1 > p.window);
+        // lse and D of this lane's 16 query rows, rows 8a + 4 half + (0..3),
+        // four at a time: the empty asm stops the compiler from loading all
+        // 32 values up front, which costs 24 registers
         float pv[16], ds[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float lr = l4[r >> 2][r & 3], dr = d4[r >> 2][r & 3];
-            const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lr * LOG2E));
-            pv[r] = pr;
-            ds[r] = pr * (dp[r] - dr);
+        for (int a = 0; a < 4; ++a) {
+            const f32x4 l4 = *(const f32x4 *)(lsel + 8 * a + 4 * half);
+            const f32x4 d4 = *(const f32x4 *)(dl + 8 * a + 4 * half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * a + e;
+                const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l4[e] * LOG2E));
+                pv[r] = pr;
+                ds[r] = pr * (dp[r] - d4[e]);
+            }
+            __asm__ volatile("" ::: "memory");
         }
         if (need_mask) {
 #pragma unroll
@@ -676,23 +643,19 @@ __global__ void __launch_bounds__(256) dkv_kernel(BParams p)
         bf16x8 pb0, pb1, db0, db1;
         pack_b(pv, pb0, pb1);
         pack_b(ds, db0, db1);
-        {
-            bf16x8 a0[NMT], a1[NMT];
-            tr_frags_all<D>(gl, tr_row, tr_col, a0, a1);
 #pragma unroll
-            for (int m = 0; m < NMT; ++m) {
-                dva[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[m], pb0, dva[m], 0, 0, 0);
-                dva[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[m], pb1, dva[m], 0, 0, 0);
-            }
+        for (int m = 0; m < NMT; ++m) {
+            bf16x8 a0, a1;
+            tr_frags<D>(gl, m, tr_row, tr_col, a0, a1);
+            dva[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, pb0, dva[m], 0, 0, 0);
+            dva[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, pb1, dva[m], 0, 0, 0);
         }
-        {
-            bf16x8 a0[NMT], a1[NMT];
-            tr_frags_all<D>(ql, tr_row, tr_col, a0, a1);
 #pragma unroll
-            for (int m = 0; m < NMT; ++m) {
-                dka[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[m], db0, dka[m], 0, 0, 0);
-                dka[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[m], db1, dka[m], 0, 0, 0);
-            }
+        for (int m = 0; m < NMT; ++m) {
+            bf16x8 a0, a1;
+            tr_frags<D>(ql, m, tr_row, tr_col, a0, a1);
+            dka[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, db0, dka[m], 0, 0, 0);
+            dka[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, db1, dka[m], 0, 0, 0);
         }
     }
     if (exists) {
@@ -710,7 +673,10 @@ hipError_t launch_bwd_v(const BwdLaunch &a, const BParams &p)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((dkv_kernel<D, NS, CAUSAL, VARLEN>), dim3(p.total), dim3(256), 0, a.stream, p);
+    // dkv at d 128: a 2-stage ring, so that two workgroups (ring plus V tiles,
+    // 64.5 KB each) share a CU's LDS; a third stage would need 80.75 KB
+    constexpr int NSK = D == 128 ? 2 : NS;
+    hipLaunchKernelGGL((dkv_kernel<D, NSK, CAUSAL, VARLEN>), dim3(p.total), dim3(256), 0, a.stream, p);
     return hipGetLastError();
 }
 
