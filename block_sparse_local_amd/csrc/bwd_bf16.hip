@@ -401,6 +401,17 @@ __global__ void __launch_bounds__(256) dq_kernel(BParams p)
             const bf16x8 va = row_frag<D>(vl, col, 2 * ks + half);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], dp, 0, 0, 0);
         }
+        // Schedule the two products' operand reads four ahead of their MFMAs
+        // (left alone, the compiler keeps one read in flight and every MFMA
+        // waits out a full LDS round trip; the registers are there, since the
+        // kernel runs two waves per SIMD at d 128 either way).
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0); // 4 LDS reads
+#pragma unroll
+        for (int x = 0; x < 2 * NKS - 4; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // 1 LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0); // the last 4 MFMAs
         // a token window also cuts blocks whose farthest pair lies beyond it
         const int dj = j > i ? j - i : i - j;
         const bool need_mask = !qvalid || pad_block || (CAUSAL && j == i) ||
