@@ -316,41 +316,46 @@ __global__ void __launch_bounds__(256) dq_kernel(BParams p)
                                        VARLEN ? last : BLK - 1, tid, wave);
     };
 
-    // this wave's query fragments, lse (log2 units) and D
+    // this wave's query and output-gradient fragments, its rows of O (for D)
+    // and lse, all loaded at once and on every lane (a lane past the sequence
+    // reads its first row, which exists, and zeroes what it read below), then
+    // the ring's first stages, and only then the wait: one memory round trip
+    // before the loop instead of one per dependent load
+    const int qread = qvalid ? qrow : 0;
     bf16x8 qf[NKS], gf[NKS];
+    u32x4 orow[NKS];
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-        u32x4 x = u32x4{0, 0, 0, 0}, y = u32x4{0, 0, 0, 0};
-        if (qvalid) {
-            x = *(const u32x4 *)(p.q + base + (size_t)qrow * RS + s * 16 + half * 8);
-            y = *(const u32x4 *)(p.dout + base + (size_t)qrow * RS + s * 16 + half * 8);
-        }
-        qf[s] = as_bf16x8(x);
-        gf[s] = as_bf16x8(y);
+        const size_t off = base + (size_t)qread * RS + s * 16 + half * 8;
+        qf[s] = as_bf16x8(*(const u32x4 *)(p.q + off));
+        gf[s] = as_bf16x8(*(const u32x4 *)(p.dout + off));
+        orow[s] = *(const u32x4 *)(p.o + off);
     }
-    const float lse2 = qvalid ? p.lse[sq.lbase + qrow] * LOG2E : 0.0f;
+    const float lse_read = p.lse[sq.lbase + qread];
+#pragma unroll
+    for (int a = 0; a < NSTAGE - 1; ++a)
+        if (a < L)
+            issue(block_at(a), a);
+    const float lse2 = qvalid ? lse_read * LOG2E : 0.0f;
     // D_t = sum_c dO_tc O_tc: this lane's half of the row (the dO fragments it
     // holds) against the same elements of O, then the other half from lane +- 32;
     // written for the key-stationary kernel, 0 on rows past the length
     float Dt = 0.0f;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-        u32x4 z = u32x4{0, 0, 0, 0};
-        if (qvalid)
-            z = *(const u32x4 *)(p.o + base + (size_t)qrow * RS + s * 16 + half * 8);
-        const bf16x8 ov = as_bf16x8(z);
+        if (!qvalid) {
+            qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+            gf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+        }
+        const bf16x8 ov = as_bf16x8(orow[s]);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             Dt = fmaf((float)gf[s][e], (float)ov[e], Dt);
+        __asm__ volatile("" : "+v"(qf[s]), "+v"(gf[s]));
     }
     Dt += __shfl_xor(Dt, 32);
     if ((VARLEN ? qvalid : exists) && half == 0)
         p.delta[sq.lbase + qrow] = Dt;
-
-#pragma unroll
-    for (int a = 0; a < NSTAGE - 1; ++a)
-        if (a < L)
-            issue(block_at(a), a);
 
     f32x16 acc[NMT];
 #pragma unroll
@@ -533,25 +538,34 @@ dkv_kernel(BParams p)
     // this wave's key and value fragments (B operands of S = Q K^T, dP = dO V^T);
     // the value fragments go to the wave's own LDS tile, each lane writing the
     // chunks it reads back in the loop (so no other lane or wave is involved),
-    // and the empty asm keeps the compiler from carrying them in registers
+    // and the empty asm keeps the compiler from carrying them in registers.
+    // Both are loaded on every lane (a lane past the sequence reads its first
+    // row and zeroes it) before the ring's first stages are issued, so that
+    // all of it costs one memory round trip rather than one per fragment.
     bf16x8 kf[NKS];
+    u32x4 vrow[NKS];
     uint8_t *const vtile = lds + NSTAGE * STAGE + wave * T::BYTES;
+    const int kread = kvalid ? krow : 0;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-        u32x4 x = u32x4{0, 0, 0, 0}, y = u32x4{0, 0, 0, 0};
-        if (kvalid) {
-            x = *(const u32x4 *)(p.k + base + (size_t)krow * RS + s * 16 + half * 8);
-            y = *(const u32x4 *)(p.v + base + (size_t)krow * RS + s * 16 + half * 8);
-        }
-        kf[s] = as_bf16x8(x);
-        *(u32x4 *)(vtile + col * T::ROW_BYTES + (((2 * s + half) ^ T::swz(col)) << 4)) = y;
+        const size_t off = base + (size_t)kread * RS + s * 16 + half * 8;
+        kf[s] = as_bf16x8(*(const u32x4 *)(p.k + off));
+        vrow[s] = *(const u32x4 *)(p.v + off);
     }
-    __asm__ volatile("" ::: "memory");
-
 #pragma unroll
     for (int a = 0; a < NSTAGE - 1; ++a)
         if (a < L)
             issue(block_at(a), a);
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+        if (!kvalid) {
+            kf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+            vrow[s] = u32x4{0, 0, 0, 0};
+        }
+        *(u32x4 *)(vtile + col * T::ROW_BYTES + (((2 * s + half) ^ T::swz(col)) << 4)) = vrow[s];
+        __asm__ volatile("" : "+v"(kf[s]));
+    }
+    __asm__ volatile("" ::: "memory");
 
     f32x16 dka[NMT], dva[NMT];
 #pragma unroll
