@@ -81,6 +81,8 @@ CASES = [
     (3, 1, 224, 64, 1, True, [0, 1, 200]),    # empty and one-token sequences
     (2, 2, 320, 128, 1, False, [320, 289]),
     (1, 3, 512, 64, 4, True, [512]),
+    (2, 2, 192, 128, 0, False, [192, 37]),    # d 128: diagonal block only, ragged
+    (3, 2, 160, 128, 2, False, [0, 1, 159]),  # d 128: empty and one-token sequences
 ]
 
 
